@@ -1,0 +1,153 @@
+"""fp64 CPU oracle for bf16 causal grouped-query attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library in ``causal_grouped_query_amd`` and imports nothing from
+it; the product never imports this package.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, one query
+row at a time).  This module only compiles it with gcc, loads it with ctypes
+and marshals numpy arrays.  Inputs are bf16 bit patterns: ``numpy.uint16`` /
+``int16`` arrays, or CPU ``torch.bfloat16`` tensors.
+
+What the oracle follows: the h3.c issue "Qwen text encoder: sequence exceeds
+Metal threadgroup memory with reference video + ref images (>=150 frames)",
+sections "Error" (the operation is the text encoder's causal GQA) and
+"Suggested fix directions" (the causal attention score row, softmax over it).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import shutil
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "oracle.c")
+LIBRARY = os.path.join(HERE, "liboracle.so")
+
+# Plain, unreordered IEEE double arithmetic: no fast-math, no FMA contraction.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+          "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile ``source`` into the shared library ``output`` with gcc."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("oracle: no C compiler (gcc) found")
+    tmp = output + ".tmp"
+    subprocess.run([cc, *CFLAGS, source, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, output)
+    return output
+
+
+def _as_bits(a, name: str) -> np.ndarray:
+    """bf16 tensor/array -> contiguous uint16 numpy array of its bit patterns."""
+    if hasattr(a, "dtype") and str(a.dtype) == "torch.bfloat16":
+        import torch
+
+        a = a.detach().to("cpu").contiguous().view(torch.int16).numpy()
+    a = np.asarray(a)
+    if a.dtype not in (np.uint16, np.int16):
+        raise TypeError(f"oracle: {name} must hold bf16 bit patterns (uint16), got {a.dtype}")
+    return np.ascontiguousarray(a).view(np.uint16)
+
+
+class Oracle:
+    """Handle on one compiled oracle library (the default one, or a test build)."""
+
+    def __init__(self, library: str = LIBRARY):
+        self.path = library
+        lib = ctypes.CDLL(library)
+        p_u16 = ctypes.POINTER(ctypes.c_uint16)
+        p_i64 = ctypes.POINTER(ctypes.c_int64)
+        p_f64 = ctypes.POINTER(ctypes.c_double)
+        i64 = ctypes.c_int64
+        lib.oracle_gqa_causal_varlen.argtypes = [p_u16, p_u16, p_u16, p_i64, i64, i64, i64, i64,
+                                                 ctypes.c_float, p_i64, i64, p_f64, p_f64,
+                                                 ctypes.c_int]
+        lib.oracle_gqa_causal_varlen.restype = ctypes.c_int
+        lib.oracle_threads.argtypes = [ctypes.c_int]
+        lib.oracle_threads.restype = ctypes.c_int
+        self._lib = lib
+
+    def threads(self, requested: int = 0) -> int:
+        """Threads a call with ``threads=requested`` uses."""
+        return int(self._lib.oracle_threads(int(requested)))
+
+    def gqa_causal_varlen(self, q, k, v, cu_seqlens, scale: float, tokens=None, threads: int = 0):
+        """Packed batch: q [T,Hq,D], k/v [T,Hkv,D] bf16 bits; cu_seqlens [n+1].
+
+        Returns ``(o, lse)``: o float64 [ntok, Hq, D], lse float64 [Hq, ntok]
+        for the packed query positions ``tokens`` (default: all T).
+        """
+        q = _as_bits(q, "q")
+        k = _as_bits(k, "k")
+        v = _as_bits(v, "v")
+        if q.ndim != 3 or k.ndim != 3 or v.shape != k.shape:
+            raise ValueError("oracle: q must be [T,Hq,D] and k, v [T,Hkv,D]")
+        T, Hq, D = q.shape
+        if k.shape[0] != T or k.shape[2] != D:
+            raise ValueError("oracle: k/v token count or head dim differs from q")
+        Hkv = k.shape[1]
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        if cu.ndim != 1 or cu.size < 2 or cu[-1] != T:
+            raise ValueError("oracle: cu_seqlens must have n+1 entries ending at T")
+        if tokens is None:
+            tokens = np.arange(T, dtype=np.int64)
+        tokens = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64).reshape(-1))
+        n = tokens.size
+        o = np.empty((n, Hq, D), dtype=np.float64)
+        lse = np.empty((Hq, n), dtype=np.float64)
+        if n == 0:
+            return o, lse
+
+        def ptr(a, t):
+            return a.ctypes.data_as(ctypes.POINTER(t))
+
+        rc = self._lib.oracle_gqa_causal_varlen(
+            ptr(q, ctypes.c_uint16), ptr(k, ctypes.c_uint16), ptr(v, ctypes.c_uint16),
+            ptr(cu, ctypes.c_int64), cu.size - 1, Hq, Hkv, D, float(np.float32(scale)),
+            ptr(tokens, ctypes.c_int64), n, ptr(o, ctypes.c_double), ptr(lse, ctypes.c_double),
+            int(threads))
+        if rc != 0:
+            raise ValueError(f"oracle: invalid arguments (code {rc})")
+        return o, lse
+
+    def gqa_causal(self, q, k, v, scale: float, tokens=None, threads: int = 0):
+        """One sequence: q [S,Hq,D], k/v [S,Hkv,D] bf16 bits -> (o, lse)."""
+        return self.gqa_causal_varlen(q, k, v, [0, int(q.shape[0])], scale, tokens=tokens,
+                                      threads=threads)
+
+
+_DEFAULT: Oracle | None = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``oracle.c``; compiled on first use if missing or stale."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        if (not os.path.exists(LIBRARY)
+                or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE)):
+            build()
+        _DEFAULT = Oracle(LIBRARY)
+    return _DEFAULT
+
+
+def gqa_causal(q, k, v, scale: float, tokens=None, threads: int = 0):
+    """Fixed-length causal GQA in fp64; see :meth:`Oracle.gqa_causal`."""
+    return default().gqa_causal(q, k, v, scale, tokens=tokens, threads=threads)
+
+
+def gqa_causal_varlen(q, k, v, cu_seqlens, scale: float, tokens=None, threads: int = 0):
+    """Packed-batch causal GQA in fp64; see :meth:`Oracle.gqa_causal_varlen`."""
+    return default().gqa_causal_varlen(q, k, v, cu_seqlens, scale, tokens=tokens,
+                                       threads=threads)
+
+
+def threads(requested: int = 0) -> int:
+    return default().threads(requested)

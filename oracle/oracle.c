@@ -1,0 +1,177 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle for bf16 causal grouped-query attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this file.  It shares no code,
+ * header, table or helper with the HIP library; neither includes the other.
+ *
+ * What it computes.  The h3.c issue "Qwen text encoder: sequence exceeds Metal
+ * threadgroup memory with reference video + ref images (>=150 frames)"
+ * (sections "Error" and "Suggested fix directions") names the operation: the
+ * text encoder's bf16 causal GQA, which forms, for every query token, the
+ * causal attention score row over all earlier tokens and takes its softmax.
+ * The tiled scheme that the same section proposes is only a faster way to the
+ * same numbers, so this oracle writes the plain definition out, one query row
+ * at a time, in double precision:
+ *
+ *   g        = h / G,  G = Hq / Hkv       (heads g*G .. g*G+G-1 share KV head g)
+ *   x_j      = scale * sum_d Q[i,h,d] * K[j,g,d]      for j = 0 .. i (local)
+ *   m        = max_j x_j
+ *   l        = sum_j exp(x_j - m)
+ *   O[i,h,:] = sum_j exp(x_j - m) / l * V[j,g,:]
+ *   LSE[h,i] = m + log(l)                               (natural log)
+ *
+ * Readings taken where the pages say nothing (they are listed, with reasons,
+ * in the design notes): the contiguous head grouping g = h / G; the diagonal
+ * is visible (key j is seen by query i iff j <= i); the softmax scale is the
+ * caller's fp32 value widened to double; LSE is the natural log of the sum of
+ * exponentials of the scaled scores; in a packed (varlen) batch positions are
+ * local to each sequence and no query sees another sequence's keys.
+ *
+ * Inputs are bf16 bit patterns (uint16); decoding bf16 to double is exact, so
+ * the only rounding is fp64's own.  Outputs stay in double.
+ *
+ * Parallelism: (token, head) items are independent; OpenMP spreads them over
+ * threads.  This changes no arithmetic: each item's sums run in the same order
+ * whatever the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double bf16_bits_to_double(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Attention of one query row over keys [first_key, last_key] (packed token
+ * indices, inclusive), i.e. the causal prefix of its own sequence.  Writes
+ * D doubles to out_o and returns the log-sum-exp.  scores: caller scratch of
+ * at least (last_key - first_key + 1) doubles. */
+static double attend_one_row(const uint16_t* q_row,      /* D values of Q[i,h,:] */
+                             const uint16_t* k, const uint16_t* v,
+                             int64_t kv_token_stride,     /* Hkv * D */
+                             int64_t g, int64_t D, double scale,
+                             int64_t first_key, int64_t last_key,
+                             double* scores, double* out_o) {
+  const int64_t n = last_key - first_key + 1;
+
+  /* scores of the causal row */
+  for (int64_t t = 0; t < n; ++t) {
+    const uint16_t* k_row = k + (first_key + t) * kv_token_stride + g * D;
+    double dot = 0.0;
+    for (int64_t d = 0; d < D; ++d)
+      dot += bf16_bits_to_double(q_row[d]) * bf16_bits_to_double(k_row[d]);
+    scores[t] = scale * dot;
+  }
+
+  /* max, then the sum of shifted exponentials */
+  double m = scores[0];
+  for (int64_t t = 1; t < n; ++t)
+    if (scores[t] > m) m = scores[t];
+  double l = 0.0;
+  for (int64_t t = 0; t < n; ++t) l += exp(scores[t] - m);
+
+  /* probability-weighted sum of the value rows */
+  for (int64_t d = 0; d < D; ++d) out_o[d] = 0.0;
+  for (int64_t t = 0; t < n; ++t) {
+    const double p = exp(scores[t] - m) / l;
+    const uint16_t* v_row = v + (first_key + t) * kv_token_stride + g * D;
+    for (int64_t d = 0; d < D; ++d) out_o[d] += p * bf16_bits_to_double(v_row[d]);
+  }
+  return m + log(l);
+}
+
+/*
+ * Packed-batch form; the fixed-length call is the case num_seqs = 1,
+ * cu_seqlens = {0, S}.
+ *
+ * q: [T, Hq, D] bf16 bits; k, v: [T, Hkv, D] bf16 bits; T = cu_seqlens[num_seqs].
+ * cu_seqlens: host int64[num_seqs + 1], cu[0] = 0, non-decreasing.
+ * tokens: the ntok packed query positions to evaluate (any order, repeats ok).
+ * o_out: [ntok, Hq, D] doubles; lse_out: [Hq, ntok] doubles.
+ * threads <= 0 means "OpenMP default".
+ * Returns 0, or a negative code for invalid arguments (nothing is written).
+ */
+int oracle_gqa_causal_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const int64_t* cu_seqlens, int64_t num_seqs,
+                             int64_t Hq, int64_t Hkv, int64_t D, float scale_f32,
+                             const int64_t* tokens, int64_t ntok,
+                             double* o_out, double* lse_out, int threads) {
+  if (!q || !k || !v || !cu_seqlens || !o_out || !lse_out || (ntok > 0 && !tokens)) return -1;
+  if (num_seqs < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv != 0) return -2;
+  if (cu_seqlens[0] != 0) return -3;
+  for (int64_t s = 0; s < num_seqs; ++s)
+    if (cu_seqlens[s + 1] < cu_seqlens[s]) return -3;
+  const int64_t T = cu_seqlens[num_seqs];
+  for (int64_t t = 0; t < ntok; ++t)
+    if (tokens[t] < 0 || tokens[t] >= T) return -4;
+
+  const int64_t G = Hq / Hkv;
+  const double scale = (double)scale_f32;
+  const int64_t n_items = ntok * Hq;
+  int status = 0;
+
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+
+#pragma omp parallel
+  {
+    int64_t longest = 0;
+    for (int64_t s = 0; s < num_seqs; ++s)
+      if (cu_seqlens[s + 1] - cu_seqlens[s] > longest) longest = cu_seqlens[s + 1] - cu_seqlens[s];
+    double* scores = (double*)malloc(sizeof(double) * (size_t)(longest > 0 ? longest : 1));
+    if (!scores) {
+#pragma omp atomic write
+      status = -5;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t item = 0; item < n_items; ++item) {
+      if (!scores) continue;
+      const int64_t ti = item / Hq;
+      const int64_t h = item % Hq;
+      const int64_t pos = tokens[ti];
+      /* the sequence holding this packed position */
+      int64_t s = 0;
+      while (!(cu_seqlens[s] <= pos && pos < cu_seqlens[s + 1])) ++s;
+      const int64_t g = h / G;
+      const uint16_t* q_row = q + (pos * Hq + h) * D;
+      lse_out[h * ntok + ti] =
+          attend_one_row(q_row, k, v, Hkv * D, g, D, scale, cu_seqlens[s], pos, scores,
+                         o_out + (ti * Hq + h) * D);
+    }
+    free(scores);
+  }
+  return status;
+}
+
+/* Fixed-length form: one sequence of S tokens. */
+int oracle_gqa_causal(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t S,
+                      int64_t Hq, int64_t Hkv, int64_t D, float scale_f32,
+                      const int64_t* tokens, int64_t ntok, double* o_out, double* lse_out,
+                      int threads) {
+  if (S < 0) return -2;
+  const int64_t cu[2] = {0, S};
+  return oracle_gqa_causal_varlen(q, k, v, cu, 1, Hq, Hkv, D, scale_f32, tokens, ntok, o_out,
+                                  lse_out, threads);
+}
+
+/* Threads an OpenMP region would use with the given request (<= 0: default). */
+int oracle_threads(int threads) {
+#ifdef _OPENMP
+  if (threads > 0) return threads;
+  return omp_get_max_threads();
+#else
+  (void)threads;
+  return 1;
+#endif
+}
