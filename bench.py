@@ -1,0 +1,215 @@
+"""Benchmark of the causal GQA forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the forward (one kernel launch) over the whole
+workload, inputs already resident in HBM.  Prints ONE JSON line with the
+throughput (causal FLOP / s: 4*D per kept (query, key) pair and query head),
+the roofline of the kernel, an oracle-match check on sampled query tokens of
+the benchmarked output, and the fp64 CPU oracle's own throughput on a bounded
+sample of the same workload.  Progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "causal GQA fwd TFLOP/s (bf16) at S=10231, % of MFMA peak; oracle-match"
+# MI355X dense bf16 MFMA peak as AMD publishes it: 256 CU x 4096 flop/clk x 2.4 GHz.
+PEAK_BF16_TFLOPS = 2516.6
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=workloads.PRIMARY, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the CPU-oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true", help="skip the oracle-match sample")
+    return ap.parse_args()
+
+
+def to_device(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def cpu_baseline(inp, w, target_s: float):
+    """fp64 oracle throughput on a bounded sample of query tokens (all heads)."""
+    import oracle
+
+    rng = np.random.Generator(np.random.PCG64(w.seed + 77))
+    T = w.total_tokens
+    starts = np.concatenate([[0], np.cumsum(w.seqlens)[:-1]])
+
+    def pair_count(tokens):
+        # visible keys of each packed token = its local position + 1
+        seq = np.searchsorted(np.cumsum(w.seqlens), tokens, side="right")
+        return int(np.sum(tokens - starts[seq] + 1))
+
+    def run(tokens):
+        t0 = time.perf_counter()
+        oracle.gqa_causal_varlen(inp["q"], inp["k"], inp["v"], w.cu_seqlens, w.scale,
+                                 tokens=tokens)
+        return time.perf_counter() - t0
+
+    calib = rng.integers(0, T, size=4)
+    dt = run(calib)
+    rate = 4 * w.head_dim * w.n_q_heads * pair_count(calib) / max(dt, 1e-6)   # flop/s
+    per_token = 4 * w.head_dim * w.n_q_heads * (T / len(w.seqlens)) / 2
+    n = int(np.clip(target_s * rate / per_token, 8, T))
+    tokens = np.sort(rng.integers(0, T, size=n))
+    log(f"cpu baseline: {n} sampled query tokens x {w.n_q_heads} heads "
+        f"(~{n * per_token / rate:.1f} s expected)")
+    dt = run(tokens)
+    flop = 4 * w.head_dim * w.n_q_heads * pair_count(tokens)
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": (f"{n} query tokens drawn uniformly from the {w.name} workload, all "
+                   f"{w.n_q_heads} heads, full causal rows; {flop:.3e} flop in {dt:.1f} s"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by KV head or sequence with no communication, see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import causal_grouped_query_amd as h3
+
+    w = workloads.WORKLOADS[args.workload]
+    log(f"workload {w.name}: seqlens={w.seqlens} Hq={w.n_q_heads} Hkv={w.n_kv_heads} "
+        f"D={w.head_dim}")
+    inp = workloads.generate(w)
+    q, k, v = to_device(inp["q"], torch), to_device(inp["k"], torch), to_device(inp["v"], torch)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.n_q_heads, w.total_tokens), dtype=torch.float32, device="cuda")
+    cu = torch.tensor(w.cu_seqlens, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        if w.varlen:
+            h3.gqa_causal_varlen_fwd(q, k, v, cu, max(w.seqlens), softmax_scale=w.scale, out=o,
+                                     lse=lse, stream=stream)
+        else:
+            h3.gqa_causal_fwd(q, k, v, softmax_scale=w.scale, out=o, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    # timed region: K steps; events on the launch stream around each launch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms
+    total_ms = starts[0].elapsed_time(ends[-1])
+    ms_per_step = total_ms / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f}"
+        f" ms/step), launch median {np.median(per_launch):.4f} ms min {per_launch.min():.4f} ms")
+
+    flop = w.causal_flop()
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    avg_launch_ms = float(per_launch.mean())
+    achieved = flop / (avg_launch_ms * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "seq_lens": list(w.seqlens),
+            "total_tokens": w.total_tokens,
+            "n_q_heads": w.n_q_heads,
+            "n_kv_heads": w.n_kv_heads,
+            "head_dim": w.head_dim,
+            "causal": True,
+            "inputs": ("N(0,1) bf16, seeded" if w.kind == "normal" else
+                       "stress: 4 N(0,1) Q/K, U(-1,1) V, 5% shared spike keys, seeded"),
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "gqa_causal_fwd_kernel",
+            "avg_launch_ms": round(avg_launch_ms, 5),
+            "algorithmic_flop_per_launch": flop,
+        },
+    }
+
+    if not args.no_check:
+        import oracle
+
+        tokens = workloads.sample_tokens(w.seqlens, 16, seed=w.seed + 1000)
+        o_ref, lse_ref = oracle.gqa_causal_varlen(inp["q"], inp["k"], inp["v"], w.cu_seqlens,
+                                                  w.scale, tokens=tokens)
+        idx = torch.from_numpy(tokens).cuda()
+        o_s = o.index_select(0, idx).double().cpu().numpy()
+        l_s = lse.index_select(1, idx).double().cpu().numpy()
+        rel = float(np.linalg.norm(o_s - o_ref) / np.linalg.norm(o_ref))
+        mx = float(np.abs(o_s - o_ref).max())
+        lmx = float(np.abs(l_s - lse_ref).max())
+        result["oracle_match"] = {
+            "tokens": int(len(tokens)), "rel_l2": rel, "max_abs": mx, "lse_abs": lmx,
+            "pass": bool(rel <= 5e-3 and mx <= 2e-2 and lmx <= 1e-3)}
+        log(f"oracle match on {len(tokens)} tokens: rel_l2={rel:.2e} max_abs={mx:.2e} "
+            f"lse_abs={lmx:.2e}")
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds)
+        log(f"cpu baseline {result['cpu_baseline']['value']:.4f} TFLOP/s on "
+            f"{result['cpu_baseline']['cores']} threads")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+"""Python binding of ``libh3attn.so``: the MI355X causal grouped-query attention forward.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels behind the C ABI in ``include/h3attn.h``; PyTorch supplies device
+memory and the current HIP stream.  There is no CPU fallback: if the library
+is missing or the device is not a gfx950, calls raise.
+
+    o, lse = gqa_causal_fwd(q, k, v)              # q [S,Hq,D], k/v [S,Hkv,D] bf16 on cuda
+    o, lse = gqa_causal_varlen_fwd(q, k, v, cu_seqlens, max_seqlen)
+
+The operation is the text encoder's bf16 causal GQA of the h3.c issue "Qwen
+text encoder: sequence exceeds Metal threadgroup memory with reference video +
+ref images (>=150 frames)" (section "Error"), computed with a tiled kernel
+whose on-chip memory does not grow with the sequence ("Suggested fix
+directions").
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG_DIR, "libh3attn.so")
+
+# status codes (include/h3attn.h)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_SCALE, ERR_LAUNCH, ERR_DEVICE = range(8)
+
+EXPORTED = ("h3attn_gqa_causal_fwd", "h3attn_gqa_causal_varlen_fwd", "h3attn_status_string",
+            "h3attn_version", "h3attn_lds_bytes")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class H3AttnError(RuntimeError):
+    """A nonzero status from the C ABI."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"h3attn: {message} (status {status})")
+        self.status = status
+
+
+def load_library(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load the HIP library (once) and declare the C signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None and path == LIBRARY:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"h3attn: HIP library {path} is not built; run "
+                "`python -c 'import __graft_entry__ as g; g.build()'` "
+                "or `python -m causal_grouped_query_amd.build`")
+        lib = ctypes.CDLL(path)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.h3attn_gqa_causal_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
+        lib.h3attn_gqa_causal_fwd.restype = i32
+        lib.h3attn_gqa_causal_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                     i32, i32, f32, vp]
+        lib.h3attn_gqa_causal_varlen_fwd.restype = i32
+        lib.h3attn_status_string.argtypes = [i32]
+        lib.h3attn_status_string.restype = ctypes.c_char_p
+        lib.h3attn_version.argtypes = []
+        lib.h3attn_version.restype = i32
+        lib.h3attn_lds_bytes.argtypes = [i32, i32]
+        lib.h3attn_lds_bytes.restype = i32
+        if path == LIBRARY:
+            _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().h3attn_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load_library().h3attn_version())
+
+
+def lds_bytes(head_dim: int, group: int) -> int:
+    return int(load_library().h3attn_lds_bytes(int(head_dim), int(group)))
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise H3AttnError(status, status_string(status))
+
+
+def _stream_handle(stream, device):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_tensors(q, k, v):
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError(f"h3attn: {name} must be a torch.bfloat16 tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"h3attn: {name} must live on a GPU (got {t.device})")
+        if not t.is_contiguous():
+            raise ValueError(f"h3attn: {name} must be contiguous")
+        if t.dim() != 3:
+            raise ValueError(f"h3attn: {name} must be [tokens, heads, head_dim]")
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
+        raise ValueError("h3attn: shapes must be q [T,Hq,D], k and v [T,Hkv,D]")
+    if not (q.device == k.device == v.device):
+        raise ValueError("h3attn: q, k, v must be on one device")
+
+
+def _outputs(q, out, lse, return_lse):
+    import torch
+
+    T, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("h3attn: out must be a contiguous bf16 tensor shaped like q")
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (Hq, T) or lse.dtype != torch.float32
+                              or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("h3attn: lse must be a contiguous float32 tensor [Hq, T]")
+    return out, lse
+
+
+def gqa_causal_fwd(q, k, v, softmax_scale: float | None = None, out=None, lse=None,
+                   return_lse: bool = True, stream=None):
+    """Causal GQA forward of one sequence.
+
+    q [S, Hq, D], k and v [S, Hkv, D]: contiguous bf16 tensors on the GPU.
+    Returns ``(o, lse)``: o [S, Hq, D] bf16 and lse [Hq, S] float32 (natural
+    log-sum-exp of the scaled scores; ``None`` if ``return_lse`` is false and
+    no ``lse`` buffer is passed).  ``softmax_scale`` defaults to 1/sqrt(D).
+    The work is enqueued on ``stream`` (default: torch's current stream).
+    """
+    _check_tensors(q, k, v)
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    out, lse = _outputs(q, out, lse, return_lse)
+    lib = load_library()
+    rc = lib.h3attn_gqa_causal_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr() if lse is not None else None, S, Hq, Hkv, D,
+                                   scale, _stream_handle(stream, q.device))
+    _check(rc)
+    return out, lse
+
+
+def gqa_causal_varlen_fwd(q, k, v, cu_seqlens, max_seqlen: int,
+                          softmax_scale: float | None = None, out=None, lse=None,
+                          return_lse: bool = True, stream=None):
+    """Causal GQA forward of a packed batch of independent sequences.
+
+    q [T, Hq, D], k and v [T, Hkv, D] bf16 on the GPU; ``cu_seqlens`` an int32
+    GPU tensor [num_seqs + 1] of offsets (cu[0] = 0, cu[-1] = T);
+    ``max_seqlen`` bounds every sequence length.  Returns ``(o, lse)`` with
+    lse [Hq, T] indexed by packed token.
+    """
+    import torch
+
+    _check_tensors(q, k, v)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 \
+            or cu_seqlens.device != q.device or cu_seqlens.dim() != 1 \
+            or not cu_seqlens.is_contiguous():
+        raise ValueError("h3attn: cu_seqlens must be a contiguous int32 tensor on q's device")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    out, lse = _outputs(q, out, lse, return_lse)
+    lib = load_library()
+    rc = lib.h3attn_gqa_causal_varlen_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, cu_seqlens.data_ptr(),
+        cu_seqlens.numel() - 1, T, int(max_seqlen), Hq, Hkv, D, scale,
+        _stream_handle(stream, q.device))
+    _check(rc)
+    return out, lse
+
+
+__all__ = ["gqa_causal_fwd", "gqa_causal_varlen_fwd", "status_string", "version", "lds_bytes",
+           "load_library", "H3AttnError", "LIBRARY", "EXPORTED"]

@@ -1,0 +1,193 @@
+// h3attn.hip -- host side of the C ABI declared in include/h3attn.h:
+// argument checks, kernel-instance selection, grid planning and launch.
+//
+// The operation is the causal GQA of the h3.c issue "Qwen text encoder:
+// sequence exceeds Metal threadgroup memory with reference video + ref images
+// (>=150 frames)" (section "Error"); where that kernel aborted the run when a
+// sequence's score row did not fit in threadgroup memory, these entry points
+// have no length-dependent capacity check at all: the kernel's LDS use is
+// fixed by (D, G).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "gqa_fwd_kernel.hpp"
+#include "h3attn.h"
+
+namespace {
+
+using h3attn::FwdConfig;
+using h3attn::FwdParams;
+
+constexpr int kWaves = 8;       // waves per workgroup: 2 per SIMD
+constexpr int kKeysPerTile = 64;
+
+template <int D, int G>
+using Cfg = FwdConfig<D, G, kWaves, kKeysPerTile>;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+bool device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+  if (dev >= kMaxDevices) return false;
+  int st = g_device_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+template <int D, int G, bool VARLEN>
+int launch(FwdParams p, hipStream_t stream) {
+  using C = Cfg<D, G>;
+  p.n_qblk = (p.seq_len + C::TOK_WG - 1) / C::TOK_WG;
+  const long long blocks = (long long)p.n_qblk * p.hkv * p.num_seqs;
+  if (blocks == 0) return H3ATTN_OK;
+  if (blocks > 0x7fffffffLL) return H3ATTN_ERR_SHAPE;
+  hipLaunchKernelGGL((h3attn::gqa_causal_fwd_kernel<C, VARLEN>), dim3((unsigned)blocks),
+                     dim3(C::THREADS), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
+}
+
+template <bool VARLEN>
+int dispatch(int D, int G, const FwdParams& p, hipStream_t stream) {
+  if (D == 128) {
+    switch (G) {
+      case 1: return launch<128, 1, VARLEN>(p, stream);
+      case 2: return launch<128, 2, VARLEN>(p, stream);
+      case 4: return launch<128, 4, VARLEN>(p, stream);
+      case 8: return launch<128, 8, VARLEN>(p, stream);
+    }
+  } else if (D == 64) {
+    switch (G) {
+      case 1: return launch<64, 1, VARLEN>(p, stream);
+      case 2: return launch<64, 2, VARLEN>(p, stream);
+      case 4: return launch<64, 4, VARLEN>(p, stream);
+      case 8: return launch<64, 8, VARLEN>(p, stream);
+    }
+  }
+  return H3ATTN_ERR_UNSUPPORTED;
+}
+
+// Checks shared by both entry points; returns a status.
+// With zero tokens there is no memory to point at, so NULL tensors are accepted then.
+int check_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 long long tokens, int Hq, int Hkv, int D, float scale) {
+  if (tokens > 0 && (!q || !k || !v || !o)) return H3ATTN_ERR_NULL;
+  if (tokens < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return H3ATTN_ERR_SHAPE;
+  if (tokens * (long long)Hq * (long long)D >= (1LL << 31)) return H3ATTN_ERR_SHAPE;
+  const int G = Hq / Hkv;
+  if ((D != 64 && D != 128) || (G != 1 && G != 2 && G != 4 && G != 8))
+    return H3ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
+    return H3ATTN_ERR_ALIGN;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return H3ATTN_ERR_SCALE;
+  return H3ATTN_OK;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" {
+
+int h3attn_gqa_causal_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int S, int Hq, int Hkv, int D, float softmax_scale, void* hip_stream) {
+  const int rc = check_common(q, k, v, o, lse, S, Hq, Hkv, D, softmax_scale);
+  if (rc != H3ATTN_OK) return rc;
+  if (S == 0) return H3ATTN_OK;
+  if (!device_ok()) return H3ATTN_ERR_DEVICE;
+  FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.cu_seqlens = nullptr;
+  p.seq_len = S;
+  p.total_tokens = S;
+  p.num_seqs = 1;
+  p.hq = Hq;
+  p.hkv = Hkv;
+  p.scale_log2 = softmax_scale * kLog2e;
+  return dispatch<false>(D, Hq / Hkv, p, static_cast<hipStream_t>(hip_stream));
+}
+
+int h3attn_gqa_causal_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const int32_t* cu_seqlens, int num_seqs, int total_tokens,
+                                 int max_seqlen, int Hq, int Hkv, int D, float softmax_scale,
+                                 void* hip_stream) {
+  const int rc = check_common(q, k, v, o, lse, total_tokens, Hq, Hkv, D, softmax_scale);
+  if (rc != H3ATTN_OK) return rc;
+  if (num_seqs < 0 || max_seqlen < 0) return H3ATTN_ERR_SHAPE;
+  if (num_seqs == 0) return total_tokens == 0 ? H3ATTN_OK : H3ATTN_ERR_SHAPE;
+  if (!cu_seqlens) return H3ATTN_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return H3ATTN_ERR_ALIGN;
+  if (total_tokens == 0 || max_seqlen == 0) return H3ATTN_OK;
+  if (!device_ok()) return H3ATTN_ERR_DEVICE;
+  FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.seq_len = max_seqlen < total_tokens ? max_seqlen : total_tokens;
+  p.total_tokens = total_tokens;
+  p.num_seqs = num_seqs;
+  p.hq = Hq;
+  p.hkv = Hkv;
+  p.scale_log2 = softmax_scale * kLog2e;
+  return dispatch<true>(D, Hq / Hkv, p, static_cast<hipStream_t>(hip_stream));
+}
+
+const char* h3attn_status_string(int status) {
+  switch (status) {
+    case H3ATTN_OK: return "ok";
+    case H3ATTN_ERR_NULL: return "a required pointer is NULL";
+    case H3ATTN_ERR_SHAPE:
+      return "invalid shape: negative size, Hq not a multiple of Hkv, inconsistent offsets, "
+             "or tokens*Hq*D >= 2^31";
+    case H3ATTN_ERR_UNSUPPORTED:
+      return "unsupported configuration: head dim must be 64 or 128 and Hq/Hkv 1, 2, 4 or 8";
+    case H3ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case H3ATTN_ERR_SCALE: return "softmax_scale must be finite and > 0";
+    case H3ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
+    case H3ATTN_ERR_DEVICE: return "no usable gfx950 device is current";
+    default: return "unknown status";
+  }
+}
+
+int h3attn_version(void) { return 100; }
+
+int h3attn_lds_bytes(int D, int G) {
+  if (D == 128) {
+    switch (G) {
+      case 1: return Cfg<128, 1>::LDS_BYTES;
+      case 2: return Cfg<128, 2>::LDS_BYTES;
+      case 4: return Cfg<128, 4>::LDS_BYTES;
+      case 8: return Cfg<128, 8>::LDS_BYTES;
+    }
+  } else if (D == 64) {
+    switch (G) {
+      case 1: return Cfg<64, 1>::LDS_BYTES;
+      case 2: return Cfg<64, 2>::LDS_BYTES;
+      case 4: return Cfg<64, 4>::LDS_BYTES;
+      case 8: return Cfg<64, 8>::LDS_BYTES;
+    }
+  }
+  return -1;
+}
+
+}  // extern "C"

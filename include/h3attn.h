@@ -1,0 +1,118 @@
+/*
+ * h3attn.h -- C ABI of the MI355X (gfx950) causal grouped-query attention
+ * forward.
+ *
+ * The operation.  The h3.c issue "Qwen text encoder: sequence exceeds Metal
+ * threadgroup memory with reference video + ref images (>=150 frames)" traces
+ * a failure of the text encoder's bf16 causal GQA ("Error" section) to a kernel
+ * that kept a whole causal score row of the sequence in threadgroup memory, and
+ * proposes tiling the score computation so that on-chip memory holds one tile
+ * at a time ("Suggested fix directions").  This library computes that
+ * operation with an on-chip footprint that does not depend on the sequence
+ * length: for every query token i and query head h,
+ *
+ *     g        = h / (Hq / Hkv)                   query heads g*G..g*G+G-1 share KV head g
+ *     x_j      = softmax_scale * <Q[i,h,:], K[j,g,:]>,   j = 0..i   (diagonal included)
+ *     O[i,h,:] = sum_j softmax_j(x) * V[j,g,:]
+ *     LSE[h,i] = log(sum_j exp(x_j))              natural log of the scaled scores
+ *
+ * Arithmetic: bf16 products with fp32 accumulation; the softmax weights are
+ * rounded to bf16 before they multiply V; O is rounded to bf16 (nearest even).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are DEVICE pointers (memory the caller allocated on the current
+ *     HIP device), dense and row-major in the shapes given; the caller owns
+ *     them.  The library allocates nothing and keeps no per-call state.
+ *   - The call enqueues work on `hip_stream` (NULL: the null stream) and
+ *     returns without waiting; the caller synchronises.
+ *   - Arguments are checked on the host before any device work.  On any
+ *     nonzero status nothing was enqueued and no output byte was written.
+ *   - There is no limit on the sequence length other than 32-bit indexing:
+ *     tokens * Hq * D < 2^31.  There is no capacity error.
+ *   - Calls into the library from several host threads are safe.
+ */
+#ifndef H3ATTN_H
+#define H3ATTN_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define H3ATTN_API __attribute__((visibility("default")))
+#else
+#define H3ATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum {
+  H3ATTN_OK = 0,
+  H3ATTN_ERR_NULL = 1,        /* a required pointer is NULL (tensors of a nonempty call, offsets) */
+  H3ATTN_ERR_SHAPE = 2,       /* negative size, Hq not a multiple of Hkv, offsets inconsistent,
+                                 or tokens * Hq * D >= 2^31 */
+  H3ATTN_ERR_UNSUPPORTED = 3, /* head dim not 64 or 128, or group size Hq/Hkv not 1, 2, 4 or 8 */
+  H3ATTN_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+  H3ATTN_ERR_SCALE = 5,       /* softmax_scale not finite or not > 0 */
+  H3ATTN_ERR_LAUNCH = 6,      /* the HIP kernel launch failed (hipGetLastError) */
+  H3ATTN_ERR_DEVICE = 7       /* no usable gfx950 device is current */
+} h3attn_status;
+
+/*
+ * Fixed-length causal GQA forward over one sequence of S tokens.
+ *
+ *   q    [S, Hq,  D] bf16   (input)
+ *   k    [S, Hkv, D] bf16   (input)
+ *   v    [S, Hkv, D] bf16   (input)
+ *   o    [S, Hq,  D] bf16   (output)
+ *   lse  [Hq, S]     fp32   (output; may be NULL when the caller does not need it)
+ *
+ * S >= 0 (S == 0 is a no-op returning H3ATTN_OK; the tensor pointers may then
+ * be NULL); Hq % Hkv == 0 with
+ * Hq / Hkv in {1, 2, 4, 8}; D in {64, 128}; softmax_scale finite and > 0
+ * (usually 1/sqrt(D)).  q, k, v, o and lse must not overlap.
+ * hip_stream is a hipStream_t (NULL: the null stream).
+ */
+H3ATTN_API int h3attn_gqa_causal_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int S, int Hq, int Hkv, int D, float softmax_scale, void* hip_stream);
+
+/*
+ * Packed variable-length causal GQA forward: num_seqs independent sequences
+ * concatenated along the token axis.  Positions are local to each sequence and
+ * no query attends to another sequence's keys.
+ *
+ *   q    [T, Hq,  D] bf16   k, v [T, Hkv, D] bf16   o [T, Hq, D] bf16
+ *   lse  [Hq, T] fp32, indexed by packed token (may be NULL)
+ *   cu_seqlens  DEVICE int32[num_seqs + 1]: cu[0] = 0, non-decreasing,
+ *               cu[num_seqs] = T = total_tokens.  Sequence s holds packed
+ *               tokens cu[s] .. cu[s+1]-1; empty sequences are allowed.
+ *   max_seqlen  an upper bound on cu[s+1] - cu[s] over all s.
+ *
+ * The offsets live on the device and are not read on the host.  The kernel
+ * clamps each sequence to [0, T] and to max_seqlen, so invalid offsets give
+ * unspecified (but in-bounds) results, never an out-of-bounds access.
+ * total_tokens == 0 is a no-op (tensor pointers may then be NULL); so is
+ * max_seqlen == 0.
+ */
+H3ATTN_API int h3attn_gqa_causal_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const int32_t* cu_seqlens, int num_seqs, int total_tokens,
+                                 int max_seqlen, int Hq, int Hkv, int D, float softmax_scale,
+                                 void* hip_stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+H3ATTN_API const char* h3attn_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+H3ATTN_API int h3attn_version(void);
+
+/* Size in bytes of the LDS (on-chip shared memory) one workgroup of the kernel
+ * instance for head dim D and group size G uses, or -1 if the pair is
+ * unsupported.  It does not depend on the sequence length. */
+H3ATTN_API int h3attn_lds_bytes(int D, int G);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3ATTN_H */
