@@ -46,6 +46,10 @@ class H3AttnError(RuntimeError):
 def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     """Load the HIP library (once) and declare the C signatures."""
     global _lib
+    # torch ships its own HIP runtime; load it first so that this library binds to the
+    # same runtime instance (same device state, streams and allocations) as torch.
+    import torch  # noqa: F401
+
     with _lock:
         if _lib is not None and path == LIBRARY:
             return _lib

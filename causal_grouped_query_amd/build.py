@@ -50,7 +50,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     noise = "packed-fp32-ops"  # the host pass does not know this device feature
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs[:40]))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
     os.replace(tmp, LIBRARY)

@@ -51,9 +51,15 @@
 //    mask (key > token -> -inf).  Keys past the sequence end are zero-filled
 //    in LDS so no row ever reads memory outside its sequence.
 //
-//  * K/V tiles are double-buffered: the next tile's global loads are issued
-//    before the current tile's MFMAs and written to the other LDS stage
-//    after them; one barrier per tile.
+//  * Two wave groups per workgroup, offset by half a tile.  Waves w and
+//    w + NW/2 run on the same SIMD.  Between two barriers, group 0 does the
+//    scores, softmax and P.V of tile t; group 1 does the softmax and P.V of
+//    tile t-1 and then the scores of tile t.  While one wave of a SIMD issues
+//    MFMAs the other issues softmax VALU work, instead of both waves hitting
+//    the MFMA pipe and then the VALU together.  The next tile's global loads
+//    are issued at the start of the interval and written to LDS at its end;
+//    one barrier per tile.  K tiles are double-buffered and V tiles
+//    triple-buffered, since group 1 reads a V tile one interval after group 0.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -106,10 +112,13 @@ struct FwdConfig {
   static constexpr int CHUNKS_ROW = D / 8;     // 16-byte chunks in one K/V row
   static constexpr int TILE_ELEMS = BN * D;    // bf16 elements of one K (or V) tile
   static constexpr int CHUNKS_PER_THREAD = BN * CHUNKS_ROW / THREADS;
-  static constexpr int LDS_BYTES = 2 /*stages*/ * 2 /*K and V*/ * TILE_ELEMS * 2;
+  static constexpr int K_STAGES = 2;
+  static constexpr int V_STAGES = 3;
+  static constexpr int LDS_BYTES = (K_STAGES + V_STAGES) * TILE_ELEMS * 2;
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
   static_assert(BN % 32 == 0, "KV tile is a whole number of 32-key MFMA blocks");
+  static_assert(NW % 2 == 0, "two wave groups");
   static_assert((BN * CHUNKS_ROW) % THREADS == 0, "tile fill divides evenly over threads");
 };
 
@@ -141,11 +150,19 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   constexpr int NDB = D / 32;    // 32-row d blocks of O^T
   constexpr int NKS = BN / 16;   // 16-key steps of the P.V contraction
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][C::TILE_ELEMS];  // [stage][K,V]
+  // K tiles double-buffered, V tiles triple-buffered (the lagging wave group reads a V tile
+  // one barrier interval after the leading group), all [key][d] with swizzled chunks.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::K_STAGES][C::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[C::V_STAGES][C::TILE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  // Waves w and w + NW/2 share a SIMD.  Group 0 (the first half) runs each tile as
+  // scores -> softmax -> P.V inside one barrier interval; group 1 runs the softmax and P.V
+  // of the previous tile first and the scores of the current tile last, so on every SIMD
+  // one wave's MFMA work overlaps the other wave's softmax (VALU) work.
+  const int group = wave / (C::NW / 2);
   const int half = lane >> 5;    // which 8-wide slice of a 16-wide contraction step
   const int col = lane & 31;     // MFMA column = this lane's query row within the wave
 
@@ -197,6 +214,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
   float m_run = -1e30f;   // running max (log2 units, scaled); finite so exp2(m_run - x) = 0
   float l_run = 0.0f;     // this lane's partial row sum (its 16 keys per block)
+  f32x16 s[NKB];          // scores of the tile between its Q.K^T and its softmax
 
   // ---- K/V tile fill: each thread moves CHUNKS_PER_THREAD 16-byte chunks of K and of V
   const int kv_stride = p.hkv * D;
@@ -220,126 +238,136 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
       }
     }
   };
-  auto store_tile = [&](int stage) {
+  auto store_tile = [&](uint16_t* kdst, uint16_t* vdst) {
 #pragma unroll
     for (int i = 0; i < C::CHUNKS_PER_THREAD; ++i) {
       const int id = i * C::THREADS + tid;
       const int key = id / C::CHUNKS_ROW;
       const int chunk = id % C::CHUNKS_ROW;
       const int off = key * D + lds_chunk(key, chunk) * 8;
-      *(u32x4*)&smem[stage][0][off] = kreg[i];
-      *(u32x4*)&smem[stage][1][off] = vreg[i];
+      *(u32x4*)&kdst[off] = kreg[i];
+      *(u32x4*)&vdst[off] = vreg[i];
     }
   };
 
-  // per-lane LDS offsets (elements) that do not depend on the tile
-  // K fragment of key block kb, d step ds: row 32*kb + col, logical chunk 2*ds + half
   // V^T fragment (transposing read): within each 16-lane group, source lane i reads
   // key kbase + i/4, d = dbase + 4*(i%4) .. +3
   const int grp = lane >> 4;           // 16-lane group
   const int gi = lane & 15;
-  const int v_key_in_quad = gi >> 2;   // b: which of the 4 keys this lane reads
-  const int v_d_in_blk = 4 * (gi & 3); // 4a: d offset inside the 16-wide block
+  const int v_key_in_quad = gi >> 2;   // which of the 4 keys this lane reads
+  const int v_d_in_blk = 4 * (gi & 3); // d offset inside the 16-wide block
   const int v_dgrp = 16 * (grp & 1);   // lanes 0-15/32-47 cover d 0-15 of a 32-block, others 16-31
   const int v_ghalf = grp >> 1;        // lanes 32-63 take the second 4-key quads
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int stage = kt & 1;
-    const bool more = kt + 1 < n_tiles;
-    if (more) load_tile(kt + 1);
-
-    if (kt * BN <= w_last) {
-      const uint16_t* ks_lds = smem[stage][0];
-      const uint16_t* vs_lds = smem[stage][1];
-
-      // S^T = K Q^T
-      f32x16 s[NKB];
+  // S^T = K Q^T for tile kt (K tile in `ks_lds`)
+  auto scores = [&](const uint16_t* ks_lds) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-        const int key = 32 * kb + col;
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+      const int key = 32 * kb + col;
 #pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, *(const u32x4*)(ks_lds + key * D + lds_chunk(key, 2 * ds + half) * 8));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], s[kb], 0, 0, 0);
-        }
+      for (int ds = 0; ds < NDS; ++ds) {
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, *(const u32x4*)(ks_lds + key * D + lds_chunk(key, 2 * ds + half) * 8));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], s[kb], 0, 0, 0);
       }
+    }
+  };
 
-      // causal mask, only on tiles that reach past the wave's first token
-      if (kt * BN + BN - 1 > wq0) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = kt * BN + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (j > my_tok) s[kb][r] = -__builtin_inff();
-          }
-      }
-
-      // row max over the tile: 16 keys per block in-lane, then the lane pair
-      float mx = -__builtin_inff();
+  // mask, online softmax and O^T += V^T P^T for tile kt (V tile in `vs_lds`)
+  auto softmax_pv = [&](int kt, const uint16_t* vs_lds) {
+    if (kt * BN + BN - 1 > wq0) {   // the tile reaches past the wave's first token
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = pair_max(mx);
-      const float mx2 = mx * p.scale_log2;
-
-      if (__builtin_amdgcn_ballot_w64(mx2 > m_run + RESCALE_SLACK) != 0) {
-        const float m_new = fmaxf(m_run, mx2);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-        m_run = m_new;
-      }
-
-      // P = exp2(S * scale*log2e - m), packed to bf16 as the B operand of P.V
-      bf16x8 pf[NKS];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        f32x8 e;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float x = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(s[ks >> 1][8 * (ks & 1) + t], p.scale_log2, -m_run));
-          l_run += x;
-          e[t] = x;
+        for (int r = 0; r < 16; ++r) {
+          const int j = kt * BN + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (j > my_tok) s[kb][r] = -__builtin_inff();
         }
-        pf[ks] = __builtin_convertvector(e, bf16x8);
-      }
-
-      // O^T += V^T P^T
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int kq0 = 16 * ks + 4 * v_ghalf + v_key_in_quad;   // key read for slots 0..3
-        const int kq1 = kq0 + 8;                                 // and for slots 4..7
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int d = 32 * db + v_dgrp + v_d_in_blk;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vs_lds + kq0 * D + lds_chunk(kq0, d >> 3) * 8 + (d & 7)));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vs_lds + kq1 * D + lds_chunk(kq1, d >> 3) * 8 + (d & 7)));
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], acc[db], 0, 0, 0);
-        }
-      }
     }
 
-    if (more) store_tile(stage ^ 1);
+    // row max over the tile: 16 keys per block in-lane, then the lane pair
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = pair_max(mx);
+    const float mx2 = mx * p.scale_log2;
+
+    if (__builtin_amdgcn_ballot_w64(mx2 > m_run + RESCALE_SLACK) != 0) {
+      const float m_new = fmaxf(m_run, mx2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      m_run = m_new;
+    }
+
+    // P = exp2(S * scale*log2e - m) as bf16: the B operand of P.V
+    bf16x8 pf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      f32x8 e;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        e[t] = __builtin_amdgcn_exp2f(
+            __builtin_fmaf(s[ks >> 1][8 * (ks & 1) + t], p.scale_log2, -m_run));
+        l_run += e[t];
+      }
+      pf[ks] = __builtin_convertvector(e, bf16x8);
+    }
+
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int kq0 = 16 * ks + 4 * v_ghalf + v_key_in_quad;   // key read for slots 0..3
+      const int kq1 = kq0 + 8;                                 // and for slots 4..7
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = 32 * db + v_dgrp + v_d_in_blk;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vs_lds + kq0 * D + lds_chunk(kq0, d >> 3) * 8 + (d & 7)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vs_lds + kq1 * D + lds_chunk(kq1, d >> 3) * 8 + (d & 7)));
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], acc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(k_lds[0], v_lds[0]);
+  __syncthreads();
+
+  int ks_cur = 0, vs_cur = 0, vs_prev = C::V_STAGES - 1;
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const bool more = kt + 1 < n_tiles;
+    if (more) load_tile(kt + 1);
+
+    if (group == 0) {
+      if (kt * BN <= w_last) {
+        scores(k_lds[ks_cur]);
+        softmax_pv(kt, v_lds[vs_cur]);
+      }
+    } else {
+      if (kt > 0 && (kt - 1) * BN <= w_last) softmax_pv(kt - 1, v_lds[vs_prev]);
+      if (kt * BN <= w_last) scores(k_lds[ks_cur]);
+    }
+
+    const int ks_next = ks_cur ^ 1;
+    const int vs_next = (vs_cur + 1 == C::V_STAGES) ? 0 : vs_cur + 1;
+    if (more) store_tile(k_lds[ks_next], v_lds[vs_next]);
     __syncthreads();
+    ks_cur = ks_next;
+    vs_prev = vs_cur;
+    vs_cur = vs_next;
   }
+  if (group == 1 && (n_tiles - 1) * BN <= w_last) softmax_pv(n_tiles - 1, v_lds[vs_prev]);
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2
   const float l_tot = pair_sum(l_run);
