@@ -34,7 +34,7 @@
 //    share one LDS layout and one fill path.
 //
 //  * LDS rows are swizzled at 16-byte granularity (chunk ^ f(key)) so the
-//    K reads (8 keys, one chunk) and the transposing V reads (4 keys, two
+//    K reads (16 keys, one chunk) and the transposing V reads (4 keys, four
 //    chunks) hit distinct banks.
 //
 //  * Online softmax in the log2 domain (exp2 with scale*log2(e) folded in).
@@ -51,19 +51,22 @@
 //    mask (key > token -> -inf).  Keys past the sequence end are zero-filled
 //    in LDS so no row ever reads memory outside its sequence.
 //
-//  * Two wave groups per workgroup, offset by half a tile.  Waves w and
-//    w + NW/2 run on the same SIMD.  Between two barriers, group 0 does the
-//    scores, softmax and P.V of tile t; group 1 does the softmax and P.V of
-//    tile t-1 and then the scores of tile t.  While one wave of a SIMD issues
-//    MFMAs the other issues softmax VALU work, instead of both waves hitting
-//    the MFMA pipe and then the VALU together.  The next tile's global loads
-//    are issued at the start of the interval and written to LDS at its end;
-//    one barrier per tile.  K tiles are double-buffered and V tiles
-//    triple-buffered, since group 1 reads a V tile one interval after group 0.
+//  * K/V tiles are double-buffered: the next tile's global loads are issued
+//    before the current tile's MFMAs and written to the other LDS stage
+//    after them; one barrier per tile.  The two waves that share a SIMD
+//    naturally drift apart within a tile (one holds the MFMA pipe while the
+//    other runs its softmax), so VALU and MFMA work overlap.
+//
+//  * LDS reads are software-pipelined: K fragments are read four MFMAs ahead
+//    of use and the first V^T fragments are read before the softmax, so LDS
+//    latency hides behind MFMA and VALU work (instruction order pinned with
+//    sched_group_barrier).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace h3attn {
 
@@ -112,23 +115,28 @@ struct FwdConfig {
   static constexpr int CHUNKS_ROW = D / 8;     // 16-byte chunks in one K/V row
   static constexpr int TILE_ELEMS = BN * D;    // bf16 elements of one K (or V) tile
   static constexpr int CHUNKS_PER_THREAD = BN * CHUNKS_ROW / THREADS;
-  static constexpr int K_STAGES = 2;
-  static constexpr int V_STAGES = 3;
-  static constexpr int LDS_BYTES = (K_STAGES + V_STAGES) * TILE_ELEMS * 2;
+  static constexpr int LDS_BYTES = 2 /*stages*/ * 2 /*K and V*/ * TILE_ELEMS * 2;
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
   static_assert(BN % 32 == 0, "KV tile is a whole number of 32-key MFMA blocks");
-  static_assert(NW % 2 == 0, "two wave groups");
   static_assert((BN * CHUNKS_ROW) % THREADS == 0, "tile fill divides evenly over threads");
 };
 
-// Physical 16-byte chunk of logical chunk `chunk` in LDS row `key`.  For 8
-// consecutive keys the XOR term takes 8 distinct values (conflict-free
-// 16-byte reads of one chunk down 8 keys); for 4 consecutive keys starting at
-// a multiple of 4 it takes 4 values spaced by 2 (conflict-free transposing
-// reads of two adjacent chunks down 4 keys).
+// Physical 16-byte chunk of logical chunk `chunk` in LDS row `key` (the gfx950 LDS has
+// 64 four-byte banks: one 256-byte bank row).  The XOR term is chosen so that
+//   * 16-byte reads of one logical chunk down 16 consecutive keys (the K operand: 16
+//     lanes per LDS cycle) hit 16 distinct bank quads, and
+//   * transposing 8-byte reads of 4 adjacent chunks down 4 consecutive keys (the V^T
+//     operand: 32 lanes per LDS cycle) hit 16 distinct bank quads.
+// For D = 128 a row is one bank row, so keys k and k+1 must land in different 4-chunk
+// groups (bits 2-3 of the term come from key bits 0-1).  For D = 64 two rows share a
+// bank row (key parity picks the half), so the term uses key bits 1-3.
+template <int D>
 __device__ __forceinline__ int lds_chunk(int key, int chunk) {
-  return chunk ^ (((key & 3) << 1) | ((key >> 2) & 1));
+  if constexpr (D == 128)
+    return chunk ^ (((key & 3) << 2) | ((key >> 2) & 3));
+  else
+    return chunk ^ (((key & 2) << 1) | ((key >> 2) & 3));
 }
 
 __device__ __forceinline__ float pair_max(float x) {
@@ -150,19 +158,13 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   constexpr int NDB = D / 32;    // 32-row d blocks of O^T
   constexpr int NKS = BN / 16;   // 16-key steps of the P.V contraction
 
-  // K tiles double-buffered, V tiles triple-buffered (the lagging wave group reads a V tile
-  // one barrier interval after the leading group), all [key][d] with swizzled chunks.
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::K_STAGES][C::TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[C::V_STAGES][C::TILE_ELEMS];
+  // K and V tiles, double-buffered, [key][d] with swizzled 16-byte chunks
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::TILE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  // Waves w and w + NW/2 share a SIMD.  Group 0 (the first half) runs each tile as
-  // scores -> softmax -> P.V inside one barrier interval; group 1 runs the softmax and P.V
-  // of the previous tile first and the scores of the current tile last, so on every SIMD
-  // one wave's MFMA work overlaps the other wave's softmax (VALU) work.
-  const int group = wave / (C::NW / 2);
   const int half = lane >> 5;    // which 8-wide slice of a 16-wide contraction step
   const int col = lane & 31;     // MFMA column = this lane's query row within the wave
 
@@ -214,7 +216,6 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
   float m_run = -1e30f;   // running max (log2 units, scaled); finite so exp2(m_run - x) = 0
   float l_run = 0.0f;     // this lane's partial row sum (its 16 keys per block)
-  f32x16 s[NKB];          // scores of the tile between its Q.K^T and its softmax
 
   // ---- K/V tile fill: each thread moves CHUNKS_PER_THREAD 16-byte chunks of K and of V
   const int kv_stride = p.hkv * D;
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   const uint16_t* vg = p.v + (size_t)start * kv_stride + g * D;
   u32x4 kreg[C::CHUNKS_PER_THREAD], vreg[C::CHUNKS_PER_THREAD];
 
-  auto load_tile = [&](int kt) {
+  auto load_tile = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::CHUNKS_PER_THREAD; ++i) {
       const int id = i * C::THREADS + tid;
@@ -238,46 +239,96 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
       }
     }
   };
-  auto store_tile = [&](uint16_t* kdst, uint16_t* vdst) {
+  auto store_tile = [&](uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::CHUNKS_PER_THREAD; ++i) {
       const int id = i * C::THREADS + tid;
       const int key = id / C::CHUNKS_ROW;
       const int chunk = id % C::CHUNKS_ROW;
-      const int off = key * D + lds_chunk(key, chunk) * 8;
+      const int off = key * D + lds_chunk<D>(key, chunk) * 8;
       *(u32x4*)&kdst[off] = kreg[i];
       *(u32x4*)&vdst[off] = vreg[i];
     }
   };
 
-  // V^T fragment (transposing read): within each 16-lane group, source lane i reads
-  // key kbase + i/4, d = dbase + 4*(i%4) .. +3
-  const int grp = lane >> 4;           // 16-lane group
-  const int gi = lane & 15;
-  const int v_key_in_quad = gi >> 2;   // which of the 4 keys this lane reads
-  const int v_d_in_blk = 4 * (gi & 3); // d offset inside the 16-wide block
-  const int v_dgrp = 16 * (grp & 1);   // lanes 0-15/32-47 cover d 0-15 of a 32-block, others 16-31
-  const int v_ghalf = grp >> 1;        // lanes 32-63 take the second 4-key quads
-
-  // S^T = K Q^T for tile kt (K tile in `ks_lds`)
-  auto scores = [&](const uint16_t* ks_lds) {
+  // Per-lane LDS element offsets that do not change from tile to tile.
+  // K fragment (key block kb, d step ds): row 32*kb + col, logical chunk 2*ds + half.  The
+  // swizzle term depends on key bits 0-3 only, so key blocks differ by a constant.
+  int k_off[NDS];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+  for (int ds = 0; ds < NDS; ++ds) k_off[ds] = col * D + lds_chunk<D>(col, 2 * ds + half) * 8;
+  // V^T fragment (16-key step ks, d block db), two transposing reads: within each 16-lane
+  // group, source lane i reads key kbase + i/4 and d = dbase + 4*(i%4) .. +3; the first read
+  // covers keys 16*ks + 4*(lane/32) + 0..3, the second the same keys + 8.  The swizzle term
+  // does not depend on ks, so 16-key steps differ by a constant.
+  int v_off[NDB][2];
+  {
+    const int grp = lane >> 4;
+    const int gi = lane & 15;
+    const int key0 = 4 * (grp >> 1) + (gi >> 2);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-      const int key = 32 * kb + col;
+    for (int db = 0; db < NDB; ++db) {
+      const int d = 32 * db + 16 * (grp & 1) + 4 * (gi & 3);
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, *(const u32x4*)(ks_lds + key * D + lds_chunk(key, 2 * ds + half) * 8));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], s[kb], 0, 0, 0);
+      for (int h = 0; h < 2; ++h) {
+        const int key = key0 + 8 * h;
+        v_off[db][h] = key * D + lds_chunk<D>(key, d >> 3) * 8 + (d & 7);
       }
     }
-  };
+  }
 
-  // mask, online softmax and O^T += V^T P^T for tile kt (V tile in `vs_lds`)
-  auto softmax_pv = [&](int kt, const uint16_t* vs_lds) {
-    if (kt * BN + BN - 1 > wq0) {   // the tile reaches past the wave's first token
+  constexpr int NKF = NKB * NDS;   // K fragments (= score MFMAs) per tile
+  constexpr int NVF = NKS * NDB;   // V^T fragments (= P.V MFMAs) per tile
+  constexpr int KPF = 4;           // K fragments in flight ahead of their MFMA
+  constexpr int VPF = 4;           // V^T fragments in flight ahead of their MFMA
+
+  // one KV tile: scores, mask, online softmax, P.V
+  auto compute_tile = [&](int kt, const uint16_t* ks_lds, const uint16_t* vs_lds) __attribute__((always_inline)) {
+    auto k_frag = [&](int i) __attribute__((always_inline)) {
+      const int kb = i % NKB, ds = i / NKB;
+      return __builtin_bit_cast(bf16x8, *(const u32x4*)(ks_lds + k_off[ds] + kb * 32 * D));
+    };
+    auto v_frag = [&](int i) __attribute__((always_inline)) {
+      const int ks = i / NDB, db = i % NDB;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vs_lds + v_off[db][0] + ks * 16 * D));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vs_lds + v_off[db][1] + ks * 16 * D));
+      return __builtin_bit_cast(
+          bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                        __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+    };
+
+    // S^T = K Q^T: the two key blocks alternate so consecutive MFMAs are independent; the
+    // K fragment reads run KPF MFMAs ahead
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+    bf16x8 kf[NKF];
+#pragma unroll
+    for (int i = 0; i < KPF; ++i) kf[i] = k_frag(i);
+#pragma unroll
+    for (int i = 0; i < NKF; ++i) {
+      if (i + KPF < NKF) kf[i + KPF] = k_frag(i + KPF);
+      s[i % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i / NKB], s[i % NKB], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
+#pragma unroll
+    for (int i = 0; i < NKF - KPF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, KPF, 0);
+
+    // first V^T fragments: their reads overlap the softmax below
+    bf16x8 vf[NVF];
+#pragma unroll
+    for (int i = 0; i < VPF; ++i) vf[i] = v_frag(i);
+
+    // causal mask, only on tiles that reach past the wave's first token
+    if (kt * BN + BN - 1 > wq0) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -321,53 +372,40 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
       pf[ks] = __builtin_convertvector(e, bf16x8);
     }
 
+    // O^T += V^T P^T, V^T reads running VPF MFMAs ahead
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int kq0 = 16 * ks + 4 * v_ghalf + v_key_in_quad;   // key read for slots 0..3
-      const int kq1 = kq0 + 8;                                 // and for slots 4..7
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int d = 32 * db + v_dgrp + v_d_in_blk;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vs_lds + kq0 * D + lds_chunk(kq0, d >> 3) * 8 + (d & 7)));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vs_lds + kq1 * D + lds_chunk(kq1, d >> 3) * 8 + (d & 7)));
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], acc[db], 0, 0, 0);
-      }
+    for (int i = 0; i < NVF; ++i) {
+      if (i + VPF < NVF) vf[i + VPF] = v_frag(i + VPF);
+      acc[i % NDB] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i / NDB], acc[i % NDB], 0, 0, 0);
     }
+#pragma unroll
+    for (int i = 0; i < NVF - VPF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, VPF, 0);
+  };
+
+  // one barrier interval: prefetch tile kt+1 into registers, compute tile kt from LDS stage
+  // ST, write tile kt+1 into the other stage, barrier.  Unrolled by stage so every LDS
+  // address is a per-lane base plus an immediate.
+  auto interval = [&](int kt, auto stage) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage)::value;
+    const bool more = kt + 1 < n_tiles;
+    if (more) load_tile(kt + 1);
+    if (kt * BN <= w_last) compute_tile(kt, k_lds[ST], v_lds[ST]);
+    if (more) store_tile(k_lds[ST ^ 1], v_lds[ST ^ 1]);
+    __syncthreads();
   };
 
   load_tile(0);
   store_tile(k_lds[0], v_lds[0]);
   __syncthreads();
-
-  int ks_cur = 0, vs_cur = 0, vs_prev = C::V_STAGES - 1;
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const bool more = kt + 1 < n_tiles;
-    if (more) load_tile(kt + 1);
-
-    if (group == 0) {
-      if (kt * BN <= w_last) {
-        scores(k_lds[ks_cur]);
-        softmax_pv(kt, v_lds[vs_cur]);
-      }
-    } else {
-      if (kt > 0 && (kt - 1) * BN <= w_last) softmax_pv(kt - 1, v_lds[vs_prev]);
-      if (kt * BN <= w_last) scores(k_lds[ks_cur]);
-    }
-
-    const int ks_next = ks_cur ^ 1;
-    const int vs_next = (vs_cur + 1 == C::V_STAGES) ? 0 : vs_cur + 1;
-    if (more) store_tile(k_lds[ks_next], v_lds[vs_next]);
-    __syncthreads();
-    ks_cur = ks_next;
-    vs_prev = vs_cur;
-    vs_cur = vs_next;
+  for (int kt = 0; kt < n_tiles; kt += 2) {
+    interval(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < n_tiles) interval(kt + 1, std::integral_constant<int, 1>{});
   }
-  if (group == 1 && (n_tiles - 1) * BN <= w_last) softmax_pv(n_tiles - 1, v_lds[vs_prev]);
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2
   const float l_tot = pair_sum(l_run);
