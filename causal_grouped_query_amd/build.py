@@ -53,6 +53,11 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs[:40]))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
+    # every symbol must resolve (a kernel whose host stub failed to instantiate would not)
+    chk = subprocess.run([sys.executable, "-c", f"import ctypes; ctypes.CDLL({tmp!r})"],
+                         capture_output=True, text=True)
+    if chk.returncode != 0:
+        raise RuntimeError("built library does not load:\n" + chk.stderr[-2000:])
     os.replace(tmp, LIBRARY)
     return LIBRARY
 

@@ -80,6 +80,15 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Word 3 of a raw buffer resource (no stride swizzle, 32-bit data format) for gfx9-family
+// GPUs; loads past num_records return zeros.
+constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
+
+// s_waitcnt vmcnt(0): wait until this wave's vector-memory loads, including loads that
+// write LDS directly, have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Kernel arguments (one struct, passed by value).
 struct FwdParams {
@@ -114,12 +123,13 @@ struct FwdConfig {
   static constexpr int TOK_WG = TOK_W * NW;    // tokens per workgroup
   static constexpr int CHUNKS_ROW = D / 8;     // 16-byte chunks in one K/V row
   static constexpr int TILE_ELEMS = BN * D;    // bf16 elements of one K (or V) tile
-  static constexpr int CHUNKS_PER_THREAD = BN * CHUNKS_ROW / THREADS;
+  static constexpr int TILE_PIECES = TILE_ELEMS * 2 / 1024;   // 1 KB pieces of one tile
+  static constexpr int PIECES_PER_WAVE = TILE_PIECES / NW;
   static constexpr int LDS_BYTES = 2 /*stages*/ * 2 /*K and V*/ * TILE_ELEMS * 2;
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
   static_assert(BN % 32 == 0, "KV tile is a whole number of 32-key MFMA blocks");
-  static_assert((BN * CHUNKS_ROW) % THREADS == 0, "tile fill divides evenly over threads");
+  static_assert(TILE_PIECES % NW == 0 && PIECES_PER_WAVE >= 1, "tile fill divides over waves");
 };
 
 // Physical 16-byte chunk of logical chunk `chunk` in LDS row `key` (the gfx950 LDS has
@@ -148,6 +158,27 @@ __device__ __forceinline__ float pair_max(float x) {
 __device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Issue one wave's share of a K/V tile fill: PIECES_PER_WAVE 1 KB pieces of K and of V,
+// each lane one 16-byte chunk at byte offset fill_off[n] of the tile, written to LDS at
+// byte 16*lane of the piece.  Bytes at or past `nbytes` (rows beyond the sequence) read 0.
+template <class C>
+__device__ __forceinline__ void fill_tile_lds(const uint16_t* ksrc, const uint16_t* vsrc,
+                                              int nbytes, uint16_t* kdst, uint16_t* vdst,
+                                              int wave, const unsigned* fill_off) {
+  const __amdgpu_buffer_rsrc_t kr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)ksrc, 0, nbytes, BUFFER_RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t vr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vsrc, 0, nbytes, BUFFER_RSRC_WORD3);
+#pragma unroll
+  for (int n = 0; n < C::PIECES_PER_WAVE; ++n) {
+    const int piece = (n * C::NW + wave) * 512;       // elements
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + piece), 16, fill_off[n], 0,
+                                             0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + piece), 16, fill_off[n], 0,
+                                             0, 0);
+  }
 }
 
 template <class C, bool VARLEN>
@@ -217,38 +248,27 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   float m_run = -1e30f;   // running max (log2 units, scaled); finite so exp2(m_run - x) = 0
   float l_run = 0.0f;     // this lane's partial row sum (its 16 keys per block)
 
-  // ---- K/V tile fill: each thread moves CHUNKS_PER_THREAD 16-byte chunks of K and of V
-  const int kv_stride = p.hkv * D;
+  // ---- K/V tile fill: buffer loads straight into LDS, no VGPR staging.  A tile is
+  // TILE_PIECES pieces of 1 KB; each wave moves PIECES_PER_WAVE pieces of K and as many of
+  // V.  Lane i of a piece lands at byte 16*i of it, so the lane fetches the global 16-byte
+  // chunk whose swizzled LDS position that is.  Rows past the sequence end fall outside the
+  // buffer's range and arrive as zeros.
+  const int kv_stride = p.hkv * D;                    // elements between consecutive tokens
   const uint16_t* kg = p.k + (size_t)start * kv_stride + g * D;
   const uint16_t* vg = p.v + (size_t)start * kv_stride + g * D;
-  u32x4 kreg[C::CHUNKS_PER_THREAD], vreg[C::CHUNKS_PER_THREAD];
-
-  auto load_tile = [&](int kt) __attribute__((always_inline)) {
+  unsigned fill_off[C::PIECES_PER_WAVE];              // byte offset of this lane's chunk in a tile
 #pragma unroll
-    for (int i = 0; i < C::CHUNKS_PER_THREAD; ++i) {
-      const int id = i * C::THREADS + tid;
-      const int key = id / C::CHUNKS_ROW;
-      const int chunk = id % C::CHUNKS_ROW;
-      const int j = kt * BN + key;
-      if (j < len) {
-        kreg[i] = *(const u32x4*)(kg + j * kv_stride + chunk * 8);
-        vreg[i] = *(const u32x4*)(vg + j * kv_stride + chunk * 8);
-      } else {
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < C::CHUNKS_PER_THREAD; ++i) {
-      const int id = i * C::THREADS + tid;
-      const int key = id / C::CHUNKS_ROW;
-      const int chunk = id % C::CHUNKS_ROW;
-      const int off = key * D + lds_chunk<D>(key, chunk) * 8;
-      *(u32x4*)&kdst[off] = kreg[i];
-      *(u32x4*)&vdst[off] = vreg[i];
-    }
+  for (int n = 0; n < C::PIECES_PER_WAVE; ++n) {
+    const int byte = (n * C::NW + wave) * 1024 + 16 * lane;
+    const int row = byte / (2 * D);
+    const int phys = (byte % (2 * D)) / 16;
+    const int logical = lds_chunk<D>(row, phys);      // the swizzle is an XOR: its own inverse
+    fill_off[n] = (unsigned)(row * kv_stride * 2 + logical * 16);
+  }
+  auto fill_tile = [&](int kt, uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
+    const int rows = min(len - kt * BN, BN);
+    const size_t tile0 = (size_t)kt * BN * kv_stride;
+    fill_tile_lds<C>(kg + tile0, vg + tile0, rows * kv_stride * 2, kdst, vdst, wave, fill_off);
   };
 
   // Per-lane LDS element offsets that do not change from tile to tile.
@@ -392,15 +412,14 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   // address is a per-lane base plus an immediate.
   auto interval = [&](int kt, auto stage) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage)::value;
-    const bool more = kt + 1 < n_tiles;
-    if (more) load_tile(kt + 1);
+    if (kt + 1 < n_tiles) fill_tile(kt + 1, k_lds[ST ^ 1], v_lds[ST ^ 1]);
     if (kt * BN <= w_last) compute_tile(kt, k_lds[ST], v_lds[ST]);
-    if (more) store_tile(k_lds[ST ^ 1], v_lds[ST ^ 1]);
-    __syncthreads();
+    wait_vmem();        // this wave's LDS-bound loads have landed ...
+    __syncthreads();    // ... and so have every other wave's
   };
 
-  load_tile(0);
-  store_tile(k_lds[0], v_lds[0]);
+  fill_tile(0, k_lds[0], v_lds[0]);
+  wait_vmem();
   __syncthreads();
   for (int kt = 0; kt < n_tiles; kt += 2) {
     interval(kt, std::integral_constant<int, 0>{});
