@@ -41,11 +41,53 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=workloads.PRIMARY, choices=sorted(workloads.WORKLOADS))
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target wall time of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the oracle-match sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def copy_probe(mib: int) -> None:
+    """One plain copy kernel of a known size, for scaling the HBM byte counters."""
+    import torch
+
+    n = mib * 1024 * 1024
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n}), flush=True)
+
+
+def recorded_traffic():
+    """HBM bytes per launch recorded for the current kernel source, or None.
+
+    profiles/gqa_causal_fwd_s10231_hbm_traffic.txt holds a line
+    `traffic_bytes_per_launch: N source_sha256: H`; the figure applies only while the
+    kernel sources still hash to H."""
+    import hashlib
+
+    src = os.path.join(ROOT, "causal_grouped_query_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(src)):
+        with open(os.path.join(src, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    path = os.path.join(ROOT, "profiles", "gqa_causal_fwd_s10231_hbm_traffic.txt")
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith("traffic_bytes_per_launch:"):
+                    parts = line.split()
+                    if parts[3] == h.hexdigest():
+                        return int(parts[1])
+    except (OSError, IndexError, ValueError):
+        pass
+    return None
 
 
 def to_device(bits, torch):
@@ -93,6 +135,9 @@ def cpu_baseline(inp, w, target_s: float):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by KV head or sequence with no communication, see DESIGN.md)",
@@ -178,7 +223,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic() if w.name == workloads.PRIMARY else None,
             "kernel": "gqa_causal_fwd_kernel",
             "avg_launch_ms": round(avg_launch_ms, 5),
             "algorithmic_flop_per_launch": flop,

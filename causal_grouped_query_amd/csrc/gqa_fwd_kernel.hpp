@@ -39,10 +39,10 @@
 //
 //  * Online softmax in the log2 domain (exp2 with scale*log2(e) folded in).
 //    The row max is reduced inside the lane (16 keys per key block) and then
-//    across the lane pair (l, l^32) with v_permlane32_swap.  The running max
-//    is only raised when a row's new max exceeds it by more than
+//    across the lane pair (l, l^32) with v_permlane32_swap.  A row's running
+//    max is only raised when its new max exceeds it by more than
 //    RESCALE_SLACK (in log2 units); otherwise the stale max is kept, the
-//    weights stay <= 2^RESCALE_SLACK and the O accumulator is not rescaled.
+//    weights stay <= 2^RESCALE_SLACK and that row's O is not rescaled.
 //    The final O = acc / l and LSE use the same max, so the result is the
 //    same function; only rounding differs.
 //
@@ -367,8 +367,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
     mx = pair_max(mx);
     const float mx2 = mx * p.scale_log2;
 
-    if (__builtin_amdgcn_ballot_w64(mx2 > m_run + RESCALE_SLACK) != 0) {
-      const float m_new = fmaxf(m_run, mx2);
+    // A row raises its m_run (and rescales its O and l) only when its tile max exceeds m_run
+    // by more than RESCALE_SLACK.  The decision is per row, so a row's arithmetic depends
+    // on its own scores only; the branch is skipped when no row of the wave needs it.
+    const bool raise = mx2 > m_run + RESCALE_SLACK;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = raise ? mx2 : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
