@@ -38,13 +38,16 @@
 //    chunks) hit distinct banks.
 //
 //  * Online softmax in the log2 domain (exp2 with scale*log2(e) folded in).
-//    The row max is reduced inside the lane (16 keys per key block) and then
-//    across the lane pair (l, l^32) with v_permlane32_swap.  A row's running
-//    max is only raised when its new max exceeds it by more than
-//    RESCALE_SLACK (in log2 units); otherwise the stale max is kept, the
-//    weights stay <= 2^RESCALE_SLACK and that row's O is not rescaled.
+//    The running max of a row is its max over the first KV tile; later
+//    tiles are exponentiated against it without computing their max.  Each
+//    lane sums its fp32 weights of the tile; only when a lane's tile sum
+//    exceeds WEIGHT_SUM_LIMIT (or is not finite) does the wave reduce the row
+//    maxima (in-lane, then across the lane pair (l, l^32) with
+//    v_permlane32_swap), raise the running max of the rows of the flagged
+//    lane pairs, rescale their O and l, and redo the tile's exponentials.  A
+//    row's decisions depend on its own scores only.
 //    The final O = acc / l and LSE use the same max, so the result is the
-//    same function; only rounding differs.
+//    same function whatever the max; only rounding differs.
 //
 //  * Causality: KV tiles past the workgroup's last token are never loaded;
 //    only tiles that reach past a wave's first token apply the elementwise
@@ -106,9 +109,11 @@ struct FwdParams {
   float scale_log2;            // softmax_scale * log2(e)
 };
 
-// The running max is raised only when a row's tile max exceeds it by more
-// than this many log2 units (a factor 2^8 = 256 of headroom in the weights).
-constexpr float RESCALE_SLACK = 8.0f;
+// A lane whose weights over one KV tile (32 keys of its row, each exp2 of the
+// score minus the running max) sum to more than this sends its row through
+// the max-and-rescale path.  Every weight is then at most 2^16, far inside the
+// fp32 / bf16 range, and O and l accumulate without overflow.
+constexpr float WEIGHT_SUM_LIMIT = 65536.0f;
 constexpr float LN2 = 0.693147180559945309417f;
 
 template <int D_, int G_, int NW_, int BN_>
@@ -358,21 +363,49 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
         }
     }
 
-    // row max over the tile: 16 keys per block in-lane, then the lane pair
-    float mx = -__builtin_inff();
+    // P = exp2(S * scale*log2e - m_run) as bf16 (the B operand of P.V) and this lane's
+    // fp32 sum of the weights (two chains)
+    bf16x8 pf[NKS];
+    auto exponentiate = [&]() __attribute__((always_inline)) -> float {
+      float l0 = 0.0f, l1 = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int ks = 0; ks < NKS; ++ks) {
+        f32x8 e;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = pair_max(mx);
-    const float mx2 = mx * p.scale_log2;
+        for (int t = 0; t < 8; ++t)
+          e[t] = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(s[ks >> 1][8 * (ks & 1) + t], p.scale_log2, -m_run));
+        pf[ks] = __builtin_convertvector(e, bf16x8);
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          l0 += e[t];
+          l1 += e[t + 1];
+        }
+      }
+      return l0 + l1;
+    };
 
-    // A row raises its m_run (and rescales its O and l) only when its tile max exceeds m_run
-    // by more than RESCALE_SLACK.  The decision is per row, so a row's arithmetic depends
-    // on its own scores only; the branch is skipped when no row of the wave needs it.
-    const bool raise = mx2 > m_run + RESCALE_SLACK;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float m_new = raise ? mx2 : m_run;
+    // Common case: weights against the running max as it stands.  The first tile, and
+    // any tile where some lane's weights sum past WEIGHT_SUM_LIMIT, take the max path.
+    float lsum = 0.0f;
+    uint64_t flagged = 0;
+    bool max_path = (kt == 0);
+    if (!max_path) {
+      lsum = exponentiate();
+      flagged = __builtin_amdgcn_ballot_w64(!(lsum <= WEIGHT_SUM_LIMIT));
+      max_path = flagged != 0;
+    }
+    if (max_path) {
+      // row max over the tile: 16 keys per block in-lane, then the lane pair
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = pair_max(mx);
+      // rows raised: all on the first tile, else those whose lane or partner lane flagged
+      const bool raise = kt == 0 || (((flagged >> col) | (flagged >> (col + 32))) & 1) != 0;
+      const float m_new = raise ? fmaxf(m_run, mx * p.scale_log2) : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -380,21 +413,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       m_run = m_new;
+      lsum = exponentiate();   // rows not raised get the same weights as before
     }
-
-    // P = exp2(S * scale*log2e - m) as bf16: the B operand of P.V
-    bf16x8 pf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      f32x8 e;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        e[t] = __builtin_amdgcn_exp2f(
-            __builtin_fmaf(s[ks >> 1][8 * (ks & 1) + t], p.scale_log2, -m_run));
-        l_run += e[t];
-      }
-      pf[ks] = __builtin_convertvector(e, bf16x8);
-    }
+    l_run += lsum;
 
     // O^T += V^T P^T, V^T reads running VPF MFMAs ahead
 #pragma unroll
