@@ -54,11 +54,11 @@
 //    mask (key > token -> -inf).  Keys past the sequence end are zero-filled
 //    in LDS so no row ever reads memory outside its sequence.
 //
-//  * K/V tiles are double-buffered: the next tile's global loads are issued
-//    before the current tile's MFMAs and written to the other LDS stage
-//    after them; one barrier per tile.  The two waves that share a SIMD
-//    naturally drift apart within a tile (one holds the MFMA pipe while the
-//    other runs its softmax), so VALU and MFMA work overlap.
+//  * K/V tiles go to LDS through buffer loads that write LDS directly, into a
+//    ring of three stages, two tiles ahead of the scores that read them; one
+//    barrier per tile.  The two waves that share a SIMD run the same cycle
+//    (softmax -> P.V -> next scores) with their barriers at different points
+//    of it, so while one issues MFMAs the other runs its softmax on the VALU.
 //
 //  * LDS reads are software-pipelined: K fragments are read four MFMAs ahead
 //    of use and the first V^T fragments are read before the softmax, so LDS
@@ -130,7 +130,8 @@ struct FwdConfig {
   static constexpr int TILE_ELEMS = BN * D;    // bf16 elements of one K (or V) tile
   static constexpr int TILE_PIECES = TILE_ELEMS * 2 / 1024;   // 1 KB pieces of one tile
   static constexpr int PIECES_PER_WAVE = TILE_PIECES / NW;
-  static constexpr int LDS_BYTES = 2 /*stages*/ * 2 /*K and V*/ * TILE_ELEMS * 2;
+  static constexpr int STAGES = 3;             // K/V tiles resident in LDS
+  static constexpr int LDS_BYTES = STAGES * 2 /*K and V*/ * TILE_ELEMS * 2;
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
   static_assert(BN % 32 == 0, "KV tile is a whole number of 32-key MFMA blocks");
@@ -179,10 +180,17 @@ __device__ __forceinline__ void fill_tile_lds(const uint16_t* ksrc, const uint16
 #pragma unroll
   for (int n = 0; n < C::PIECES_PER_WAVE; ++n) {
     const int piece = (n * C::NW + wave) * 512;       // elements
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + piece), 16, fill_off[n], 0,
-                                             0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + piece), 16, fill_off[n], 0,
-                                             0, 0);
+    const unsigned kl = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_void*)(kdst + piece));
+    const unsigned vl = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_void*)(vdst + piece));
+    // Issued as inline assembly so that the compiler does not track these LDS writes: it
+    // would otherwise wait for them before unrelated LDS reads of other stages.  The
+    // kernel orders them itself (wait_vmem, then a workgroup barrier, before any read).
+    // The s_nop covers the one wait state between an SALU write of M0 and its use as the
+    // LDS address of a buffer load.
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(fill_off[n]), "s"(kr), "s"(kl) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(fill_off[n]), "s"(vr), "s"(vl) : "memory", "m0");
   }
 }
 
@@ -194,9 +202,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   constexpr int NDB = D / 32;    // 32-row d blocks of O^T
   constexpr int NKS = BN / 16;   // 16-key steps of the P.V contraction
 
-  // K and V tiles, double-buffered, [key][d] with swizzled 16-byte chunks
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][C::TILE_ELEMS];
+  // K and V tiles, a ring of STAGES, [key][d] with swizzled 16-byte chunks
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::STAGES][C::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[C::STAGES][C::TILE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -307,36 +315,38 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   constexpr int KPF = 4;           // K fragments in flight ahead of their MFMA
   constexpr int VPF = 4;           // V^T fragments in flight ahead of their MFMA
 
-  // one KV tile: scores, mask, online softmax, P.V
-  auto compute_tile = [&](int kt, const uint16_t* ks_lds, const uint16_t* vs_lds) __attribute__((always_inline)) {
-    auto k_frag = [&](int i) __attribute__((always_inline)) {
-      const int kb = i % NKB, ds = i / NKB;
-      return __builtin_bit_cast(bf16x8, *(const u32x4*)(ks_lds + k_off[ds] + kb * 32 * D));
-    };
-    auto v_frag = [&](int i) __attribute__((always_inline)) {
-      const int ks = i / NDB, db = i % NDB;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(vs_lds + v_off[db][0] + ks * 16 * D));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(vs_lds + v_off[db][1] + ks * 16 * D));
-      return __builtin_bit_cast(
-          bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                        __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
-    };
+  auto k_frag = [&](const uint16_t* ks_lds, int i) __attribute__((always_inline)) {
+    const int kb = i % NKB, ds = i / NKB;
+    return __builtin_bit_cast(bf16x8, *(const u32x4*)(ks_lds + k_off[ds] + kb * 32 * D));
+  };
+  auto v_frag = [&](const uint16_t* vs_lds, int i) __attribute__((always_inline)) {
+    const int ks = i / NDB, db = i % NDB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(vs_lds + v_off[db][0] + ks * 16 * D));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(vs_lds + v_off[db][1] + ks * 16 * D));
+    return __builtin_bit_cast(
+        bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                      __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+  };
 
-    // S^T = K Q^T: the two key blocks alternate so consecutive MFMAs are independent; the
-    // K fragment reads run KPF MFMAs ahead
-    f32x16 s[NKB];
+  f32x16 s[NKB];   // raw scores of the tile whose softmax comes next
+  bf16x8 pf[NKS];  // its weights as bf16: the B operands of its P.V MFMAs
+  bf16x8 vf[NVF];  // V^T fragments, the first VPF read ahead of the P.V MFMAs
+
+  // S^T = K Q^T for one tile: the two key blocks alternate so consecutive MFMAs are
+  // independent; the K fragment reads run KPF MFMAs ahead
+  auto scores = [&](const uint16_t* ks_lds) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
     bf16x8 kf[NKF];
 #pragma unroll
-    for (int i = 0; i < KPF; ++i) kf[i] = k_frag(i);
+    for (int i = 0; i < KPF; ++i) kf[i] = k_frag(ks_lds, i);
 #pragma unroll
     for (int i = 0; i < NKF; ++i) {
-      if (i + KPF < NKF) kf[i + KPF] = k_frag(i + KPF);
+      if (i + KPF < NKF) kf[i + KPF] = k_frag(ks_lds, i + KPF);
       s[i % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i / NKB], s[i % NKB], 0, 0, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
@@ -346,12 +356,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, KPF, 0);
+  };
 
-    // first V^T fragments: their reads overlap the softmax below
-    bf16x8 vf[NVF];
-#pragma unroll
-    for (int i = 0; i < VPF; ++i) vf[i] = v_frag(i);
-
+  // causal mask and online softmax of tile kt (scores in s) -> pf, l_run, m_run
+  auto softmax = [&](int kt) __attribute__((always_inline)) {
     // causal mask, only on tiles that reach past the wave's first token
     if (kt * BN + BN - 1 > wq0) {
 #pragma unroll
@@ -363,9 +371,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
         }
     }
 
-    // P = exp2(S * scale*log2e - m_run) as bf16 (the B operand of P.V) and this lane's
-    // fp32 sum of the weights (two chains)
-    bf16x8 pf[NKS];
+    // P = exp2(S * scale*log2e - m_run) as bf16 and this lane's fp32 sum of the weights
+    // (two chains)
     auto exponentiate = [&]() __attribute__((always_inline)) -> float {
       float l0 = 0.0f, l1 = 0.0f;
 #pragma unroll
@@ -416,11 +423,13 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
       lsum = exponentiate();   // rows not raised get the same weights as before
     }
     l_run += lsum;
+  };
 
-    // O^T += V^T P^T, V^T reads running VPF MFMAs ahead
+  // O^T += V^T P^T for one tile; vf[0 .. VPF) already read, the rest run VPF MFMAs ahead
+  auto pv = [&](const uint16_t* vs_lds) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NVF; ++i) {
-      if (i + VPF < NVF) vf[i + VPF] = v_frag(i + VPF);
+      if (i + VPF < NVF) vf[i + VPF] = v_frag(vs_lds, i + VPF);
       acc[i % NDB] =
           __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i / NDB], acc[i % NDB], 0, 0, 0);
     }
@@ -432,23 +441,52 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
     __builtin_amdgcn_sched_group_barrier(0x008, VPF, 0);
   };
 
-  // one barrier interval: prefetch tile kt+1 into registers, compute tile kt from LDS stage
-  // ST, write tile kt+1 into the other stage, barrier.  Unrolled by stage so every LDS
-  // address is a per-lane base plus an immediate.
-  auto interval = [&](int kt, auto stage) __attribute__((always_inline)) {
+  // ---- tile loop.  Barrier b(j) follows the interval in which this wave's share of tile
+  // j+1 was loaded; right after it every wave issues its share of tile j+2.  A tile lives in
+  // LDS stage tile % 3: its K is read by the scores before b(tile), its V by the P.V before
+  // b(tile + 1), and the stage is refilled (tile + 3) only after b(tile + 1).
+  //
+  // Each wave runs the cycle  softmax(t) -> P.V(t) -> scores(t+1)  and the two waves that
+  // share a SIMD (w and w + NW/2) place their barrier at different points of it: group 0
+  // between softmax(t) and P.V(t), group 1 after scores(t+1).  Between two barriers one
+  // group therefore issues MFMAs (P.V then scores) while the other runs its softmax on the
+  // VALU, and the SIMD's matrix core and VALU work at the same time.
+  const int group = wave / (C::NW / 2);
+  const int t_last = (w_last >= 0) ? w_last / BN : -1;   // last tile with a visible key
+  auto sync = [&](int j) __attribute__((always_inline)) {
+    wait_vmem();        // this wave's share of tile j+1 has landed in LDS ...
+    __syncthreads();    // ... and so has every other wave's; b(j) passed
+    if (j + 2 < n_tiles) {
+      const int st = (j + 2) % 3;
+      fill_tile(j + 2, k_lds[st], v_lds[st]);
+    }
+  };
+  // loop step t on LDS stage ST = t % 3 (unrolled by stage so LDS addresses are immediates)
+  auto step = [&](int t, auto stage) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage)::value;
-    if (kt + 1 < n_tiles) fill_tile(kt + 1, k_lds[ST ^ 1], v_lds[ST ^ 1]);
-    if (kt * BN <= w_last) compute_tile(kt, k_lds[ST], v_lds[ST]);
-    wait_vmem();        // this wave's LDS-bound loads have landed ...
-    __syncthreads();    // ... and so have every other wave's
+    constexpr int SN = (ST + 1) % 3;
+    const bool mine = t <= t_last;
+    if (mine) {
+#pragma unroll
+      for (int i = 0; i < VPF; ++i) vf[i] = v_frag(v_lds[ST], i);   // overlap the softmax
+      softmax(t);
+    }
+    if (group == 0) sync(t);
+    if (mine) pv(v_lds[ST]);
+    if (t + 1 <= t_last) scores(k_lds[SN]);
+    if (group == 1 && t + 1 < n_tiles) sync(t + 1);
   };
 
   fill_tile(0, k_lds[0], v_lds[0]);
   wait_vmem();
-  __syncthreads();
-  for (int kt = 0; kt < n_tiles; kt += 2) {
-    interval(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < n_tiles) interval(kt + 1, std::integral_constant<int, 1>{});
+  __syncthreads();                                    // b(-1): tile 0 in LDS
+  if (1 < n_tiles) fill_tile(1, k_lds[1], v_lds[1]);
+  if (0 <= t_last) scores(k_lds[0]);
+  if (group == 1) sync(0);
+  for (int t = 0; t < n_tiles; t += 3) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 2 < n_tiles) step(t + 2, std::integral_constant<int, 2>{});
   }
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2
