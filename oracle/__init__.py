@@ -71,6 +71,10 @@ class Oracle:
                                                  ctypes.c_float, p_i64, i64, p_f64, p_f64,
                                                  ctypes.c_int]
         lib.oracle_gqa_causal_varlen.restype = ctypes.c_int
+        lib.oracle_gqa_causal_keyrange.argtypes = [p_u16, p_u16, p_u16, i64, i64, i64, i64,
+                                                   ctypes.c_float, i64, i64, p_i64, i64, p_f64,
+                                                   p_f64, ctypes.c_int]
+        lib.oracle_gqa_causal_keyrange.restype = ctypes.c_int
         lib.oracle_threads.argtypes = [ctypes.c_int]
         lib.oracle_threads.restype = ctypes.c_int
         self._lib = lib
@@ -123,6 +127,42 @@ class Oracle:
         return self.gqa_causal_varlen(q, k, v, [0, int(q.shape[0])], scale, tokens=tokens,
                                       threads=threads)
 
+    def gqa_causal_keyrange(self, q, k, v, scale: float, key_begin: int, key_end: int,
+                            tokens=None, threads: int = 0):
+        """One sequence, keys restricted to [key_begin, key_end) (and j <= i).
+
+        Returns ``(o, lse)`` like :meth:`gqa_causal`; rows with no key in range
+        get o = 0 and lse = -inf.
+        """
+        q = _as_bits(q, "q")
+        k = _as_bits(k, "k")
+        v = _as_bits(v, "v")
+        if q.ndim != 3 or k.ndim != 3 or v.shape != k.shape or k.shape[0] != q.shape[0] \
+                or k.shape[2] != q.shape[2]:
+            raise ValueError("oracle: q must be [S,Hq,D] and k, v [S,Hkv,D]")
+        S, Hq, D = q.shape
+        Hkv = k.shape[1]
+        if tokens is None:
+            tokens = np.arange(S, dtype=np.int64)
+        tokens = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64).reshape(-1))
+        n = tokens.size
+        o = np.empty((n, Hq, D), dtype=np.float64)
+        lse = np.empty((Hq, n), dtype=np.float64)
+        if n == 0:
+            return o, lse
+
+        def ptr(a, t):
+            return a.ctypes.data_as(ctypes.POINTER(t))
+
+        rc = self._lib.oracle_gqa_causal_keyrange(
+            ptr(q, ctypes.c_uint16), ptr(k, ctypes.c_uint16), ptr(v, ctypes.c_uint16), S, Hq,
+            Hkv, D, float(np.float32(scale)), int(key_begin), int(key_end),
+            ptr(tokens, ctypes.c_int64), n, ptr(o, ctypes.c_double), ptr(lse, ctypes.c_double),
+            int(threads))
+        if rc != 0:
+            raise ValueError(f"oracle: invalid arguments (code {rc})")
+        return o, lse
+
 
 _DEFAULT: Oracle | None = None
 
@@ -147,6 +187,37 @@ def gqa_causal_varlen(q, k, v, cu_seqlens, scale: float, tokens=None, threads: i
     """Packed-batch causal GQA in fp64; see :meth:`Oracle.gqa_causal_varlen`."""
     return default().gqa_causal_varlen(q, k, v, cu_seqlens, scale, tokens=tokens,
                                        threads=threads)
+
+
+def gqa_causal_keyrange(q, k, v, scale: float, key_begin: int, key_end: int, tokens=None,
+                        threads: int = 0):
+    """Attention over a key range; see :meth:`Oracle.gqa_causal_keyrange`."""
+    return default().gqa_causal_keyrange(q, k, v, scale, key_begin, key_end, tokens=tokens,
+                                         threads=threads)
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine attention results over disjoint key sets into the result over their union.
+
+    o_parts: [n, ntok, Hq, D], lse_parts: [n, Hq, ntok] (float64; empty parts carry
+    lse = -inf).  The softmax over a union of disjoint sets weighs part c by
+    exp(lse_c) / sum_c' exp(lse_c'), and the union's log-sum-exp is the log of that
+    sum; the largest lse is factored out so that no exponential overflows.  Rows with
+    every part empty come out as o = 0, lse = -inf.
+    Returns ``(o, lse)`` with shapes [ntok, Hq, D] and [Hq, ntok].
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)                                  # [Hq, ntok]
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(lse_parts - m_safe)                             # exp(-inf) = 0
+    total = w.sum(axis=0)                                      # [Hq, ntok]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        lse = np.where(total > 0, m_safe + np.log(total), -np.inf)
+        frac = np.where(total > 0, w / np.where(total > 0, total, 1.0), 0.0)   # [n, Hq, ntok]
+    # O[t, h, :] = sum_c frac[c, h, t] * o_parts[c, t, h, :]
+    o = (frac.transpose(0, 2, 1)[..., None] * o_parts).sum(axis=0)
+    return o, lse
 
 
 def threads(requested: int = 0) -> int:

@@ -31,6 +31,13 @@
  * Inputs are bf16 bit patterns (uint16); decoding bf16 to double is exact, so
  * the only rounding is fp64's own.  Outputs stay in double.
  *
+ * Split-KV partials (the first fix direction of the same section: the score
+ * row computed in pieces, with intermediate results in global memory) are
+ * attention restricted to a key range: oracle_gqa_causal_keyrange evaluates
+ * the same definition over keys j in [key_begin, key_end) with j <= i, giving
+ * O = 0 and LSE = -inf where that set is empty.  Merging partials is done in
+ * oracle/__init__.py (merge_partials), in double precision with numpy.
+ *
  * Parallelism: (token, head) items are independent; OpenMP spreads them over
  * threads.  This changes no arithmetic: each item's sums run in the same order
  * whatever the thread count.
@@ -163,6 +170,62 @@ int oracle_gqa_causal(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
   const int64_t cu[2] = {0, S};
   return oracle_gqa_causal_varlen(q, k, v, cu, 1, Hq, Hkv, D, scale_f32, tokens, ntok, o_out,
                                   lse_out, threads);
+}
+
+/*
+ * Key-range form (one sequence of S tokens): query token i attends to the keys
+ * j with key_begin <= j < key_end and j <= i.  Where no key qualifies the row's
+ * output is O = 0, LSE = -inf.  Same layouts and return codes as above.
+ */
+int oracle_gqa_causal_keyrange(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               int64_t S, int64_t Hq, int64_t Hkv, int64_t D, float scale_f32,
+                               int64_t key_begin, int64_t key_end,
+                               const int64_t* tokens, int64_t ntok,
+                               double* o_out, double* lse_out, int threads) {
+  if (!q || !k || !v || !o_out || !lse_out || (ntok > 0 && !tokens)) return -1;
+  if (S < 0 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv != 0) return -2;
+  for (int64_t t = 0; t < ntok; ++t)
+    if (tokens[t] < 0 || tokens[t] >= S) return -4;
+
+  const int64_t G = Hq / Hkv;
+  const double scale = (double)scale_f32;
+  const int64_t n_items = ntok * Hq;
+  int status = 0;
+
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+
+#pragma omp parallel
+  {
+    double* scores = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    if (!scores) {
+#pragma omp atomic write
+      status = -5;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t item = 0; item < n_items; ++item) {
+      if (!scores) continue;
+      const int64_t ti = item / Hq;
+      const int64_t h = item % Hq;
+      const int64_t pos = tokens[ti];
+      const int64_t g = h / G;
+      const int64_t first = key_begin > 0 ? key_begin : 0;
+      const int64_t last = (key_end - 1 < pos) ? key_end - 1 : pos;
+      double* o_row = o_out + (ti * Hq + h) * D;
+      if (first > last) {
+        for (int64_t d = 0; d < D; ++d) o_row[d] = 0.0;
+        lse_out[h * ntok + ti] = -INFINITY;
+        continue;
+      }
+      lse_out[h * ntok + ti] = attend_one_row(q + (pos * Hq + h) * D, k, v, Hkv * D, g, D,
+                                              scale, first, last, scores, o_row);
+    }
+    free(scores);
+  }
+  return status;
 }
 
 /* Threads an OpenMP region would use with the given request (<= 0: default). */

@@ -14,7 +14,10 @@ Each ``pin_*`` function takes an :class:`oracle.Oracle` and raises
 * invariants (future tokens never change earlier rows; a packed batch equals
   its sequences run one at a time; GQA equals MHA with K/V repeated),
 * the exact result (50-digit mpmath) on sampled rows, including logits large
-  enough to overflow exp() without the max shift.
+  enough to overflow exp() without the max shift,
+* for the split-KV building blocks: attention over a key range against dense
+  masked matrices, a one-key range in closed form, and the merge of partials
+  over a partition of the keys against the full result.
 
 ``tests/test_oracle_pins.py`` runs them on the real oracle and
 ``tests/test_oracle_mutations.py`` checks that each planted mistake in a copy
@@ -257,6 +260,83 @@ def pin_exact_rows_mpmath(orc):
                 assert abs(lse[h, ri] - float(el)) <= 1e-13 * max(1.0, abs(float(el))), (i, h)
 
 
+def pin_keyrange_brute_force(orc):
+    """Attention over a key range [kb, ke) (and j <= i) against dense masked matrices;
+    rows with no key in range give O = 0, LSE = -inf."""
+    cases = [  # S, Hq, Hkv, D, seed, kb, ke
+        (40, 4, 2, 16, 70, 0, 40),
+        (40, 4, 2, 16, 71, 7, 23),
+        (33, 8, 1, 8, 72, 32, 33),
+        (50, 2, 2, 64, 73, 10, 11),
+        (20, 4, 4, 16, 74, 25, 30),     # entirely past the sequence: every row empty
+    ]
+    for S, Hq, Hkv, D, seed, kb, ke in cases:
+        q, k, v = normal_inputs(seed, S, Hq, Hkv, D, sigma=1.5)
+        scale = default_scale(D)
+        o, lse = orc.gqa_causal_keyrange(q, k, v, scale, kb, ke)
+        Q, K, V = _f64(q), _f64(k), _f64(v)
+        G = Hq // Hkv
+        i_idx, j_idx = np.meshgrid(np.arange(S), np.arange(S), indexing="ij")
+        visible = (j_idx <= i_idx) & (j_idx >= kb) & (j_idx < ke)
+        for h in range(Hq):
+            g = h // G
+            X = float(np.float32(scale)) * (Q[:, h, :] @ K[:, g, :].T)
+            X = np.where(visible, X, -np.inf)
+            for i in range(S):
+                if not visible[i].any():
+                    assert lse[h, i] == -np.inf and np.all(o[i, h] == 0.0), (seed, i, h)
+                    continue
+                m = X[i].max()
+                w = np.exp(X[i] - m)
+                assert abs(lse[h, i] - (m + np.log(w.sum()))) <= 1e-12 * max(1.0, abs(m)), (i, h)
+                assert np.allclose(o[i, h], (w / w.sum()) @ V[:, g, :], rtol=1e-12, atol=1e-13)
+
+
+def pin_merge_of_key_partition(orc):
+    """Partials over a partition of the keys, merged, equal the full causal result: the
+    softmax over a union of disjoint key sets is the exp(LSE)-weighted mix of the
+    softmaxes over the parts."""
+    cases = [  # S, Hq, Hkv, D, seed, sigma, cut points
+        (64, 4, 2, 32, 80, 1.0, (16, 48)),
+        (100, 8, 2, 16, 81, 3.0, (1, 2, 50, 99)),
+        (37, 2, 1, 64, 82, 8.0, (36,)),       # large logits: merging needs the max shift
+        (48, 4, 4, 16, 83, 1.0, (0, 48)),     # empty first and last parts
+    ]
+    for S, Hq, Hkv, D, seed, sigma, cuts in cases:
+        q, k, v = normal_inputs(seed, S, Hq, Hkv, D, sigma=sigma)
+        scale = default_scale(D)
+        bounds = [0, *cuts, S]
+        parts = [orc.gqa_causal_keyrange(q, k, v, scale, a, b) for a, b in zip(bounds, bounds[1:])]
+        import oracle as _oracle
+
+        o, lse = _oracle.merge_partials(np.stack([p[0] for p in parts]),
+                                        np.stack([p[1] for p in parts]))
+        o_ref, lse_ref = orc.gqa_causal(q, k, v, scale)
+        assert np.allclose(lse, lse_ref, rtol=1e-13, atol=1e-12), seed
+        assert np.allclose(o, o_ref, rtol=1e-12, atol=1e-12), seed
+
+
+def pin_keyrange_single_key(orc):
+    """A one-key range [j, j+1): rows i >= j return V[j] exactly and LSE = scale*q.k_j
+    (the dot product exact in rational arithmetic); rows i < j are empty."""
+    S, Hq, Hkv, D, j = 24, 4, 2, 16, 9
+    q, k, v = normal_inputs(90, S, Hq, Hkv, D)
+    scale = default_scale(D)
+    o, lse = orc.gqa_causal_keyrange(q, k, v, scale, j, j + 1)
+    Q, K, V = _f64(q), _f64(k), _f64(v)
+    G = Hq // Hkv
+    for i in range(S):
+        for h in range(Hq):
+            if i < j:
+                assert lse[h, i] == -np.inf and np.all(o[i, h] == 0.0)
+                continue
+            g = h // G
+            assert np.all(o[i, h] == V[j, g]), (i, h)
+            dot = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(Q[i, h], K[j, g]))
+            exact = float(Fraction(float(np.float32(scale))) * dot)
+            assert abs(lse[h, i] - exact) <= 1e-14 * max(1.0, abs(exact)), (i, h)
+
+
 ALL_PINS = [
     pin_brute_force_dense,
     pin_torch_sdpa_float64,
@@ -269,4 +349,7 @@ ALL_PINS = [
     pin_causality,
     pin_varlen_is_concatenation,
     pin_exact_rows_mpmath,
+    pin_keyrange_brute_force,
+    pin_merge_of_key_partition,
+    pin_keyrange_single_key,
 ]

@@ -28,6 +28,12 @@ MUTANTS = {
                                   "double* scores = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));")],
     "no_max_shift": ("l += exp(scores[t] - m);", "l += exp(scores[t]);"),
     "float32_dot": ("double dot = 0.0;", "float dot = 0.0f;"),
+    "keyrange_end_inclusive": ("(key_end - 1 < pos) ? key_end - 1 : pos",
+                               "(key_end < pos) ? key_end : pos"),
+    "keyrange_begin_ignored": ("const int64_t first = key_begin > 0 ? key_begin : 0;",
+                               "const int64_t first = 0;"),
+    "keyrange_empty_lse_zero": ("lse_out[h * ntok + ti] = -INFINITY;",
+                                "lse_out[h * ntok + ti] = 0.0;"),
 }
 
 
@@ -39,8 +45,8 @@ def test_mutant_is_caught(name, tmp_path):
     with open(oracle.SOURCE) as f:
         src = f.read()
     for old, new in edits:
-        assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
-        src = src.replace(old, new)
+        assert src.count(old) >= 1, f"mutation site for {name} not found"
+        src = src.replace(old, new)   # every occurrence: both entry points share the mistake
     mutant_src = tmp_path / "oracle_mutant.c"
     mutant_src.write_text(src)
     lib = oracle.build(str(mutant_src), str(tmp_path / "liboracle_mutant.so"))
@@ -52,3 +58,43 @@ def test_mutant_is_caught(name, tmp_path):
         except (AssertionError, ValueError, FloatingPointError):
             failed.append(pin.__name__)
     assert failed, f"no pin notices the mutant {name}"
+
+
+def _merge_plain_mean(o_parts, lse_parts):
+    """Mistake: parts averaged with equal weights."""
+    import numpy as np
+
+    o = np.asarray(o_parts).mean(axis=0)
+    return o, np.log(np.exp(np.asarray(lse_parts)).sum(axis=0))
+
+
+_RIGHT_MERGE = oracle.merge_partials
+
+
+def _merge_lse_is_max(o_parts, lse_parts):
+    """Mistake: the union's LSE taken as the largest part's LSE."""
+    import numpy as np
+
+    o, _ = _RIGHT_MERGE(o_parts, lse_parts)
+    return o, np.asarray(lse_parts).max(axis=0)
+
+
+def _merge_not_renormalised(o_parts, lse_parts):
+    """Mistake: part weights exp(lse_c - max) used without dividing by their sum."""
+    import numpy as np
+
+    lse_parts = np.asarray(lse_parts)
+    m = lse_parts.max(axis=0)
+    w = np.exp(lse_parts - m)
+    o = (w.transpose(0, 2, 1)[..., None] * np.asarray(o_parts)).sum(axis=0)
+    return o, m + np.log(w.sum(axis=0))
+
+
+@pytest.mark.parametrize("wrong", [_merge_plain_mean, _merge_lse_is_max, _merge_not_renormalised],
+                         ids=lambda f: f.__name__.lstrip("_"))
+def test_wrong_merge_is_caught(wrong, monkeypatch):
+    from oracle_pins import pin_merge_of_key_partition
+
+    monkeypatch.setattr(oracle, "merge_partials", wrong)
+    with pytest.raises(AssertionError):
+        pin_merge_of_key_partition(oracle.default())
