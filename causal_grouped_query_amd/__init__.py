@@ -26,10 +26,13 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(PKG_DIR, "libh3attn.so")
 
 # status codes (include/h3attn.h)
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_SCALE, ERR_LAUNCH, ERR_DEVICE = range(8)
+(OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_SCALE, ERR_LAUNCH, ERR_DEVICE,
+ ERR_WORKSPACE) = range(9)
+MAX_SPLITS = 64
 
-EXPORTED = ("h3attn_gqa_causal_fwd", "h3attn_gqa_causal_varlen_fwd", "h3attn_status_string",
-            "h3attn_version", "h3attn_lds_bytes")
+EXPORTED = ("h3attn_gqa_causal_fwd", "h3attn_gqa_causal_varlen_fwd",
+            "h3attn_gqa_causal_splitkv_fwd", "h3attn_gqa_causal_splitkv_workspace_bytes",
+            "h3attn_status_string", "h3attn_version", "h3attn_lds_bytes")
 
 _lock = threading.Lock()
 _lib = None
@@ -65,6 +68,12 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         lib.h3attn_gqa_causal_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                                      i32, i32, f32, vp]
         lib.h3attn_gqa_causal_varlen_fwd.restype = i32
+        sz = ctypes.c_size_t
+        lib.h3attn_gqa_causal_splitkv_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                      f32, i32, vp, sz, vp]
+        lib.h3attn_gqa_causal_splitkv_fwd.restype = i32
+        lib.h3attn_gqa_causal_splitkv_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        lib.h3attn_gqa_causal_splitkv_workspace_bytes.restype = sz
         lib.h3attn_status_string.argtypes = [i32]
         lib.h3attn_status_string.restype = ctypes.c_char_p
         lib.h3attn_version.argtypes = []
@@ -190,5 +199,46 @@ def gqa_causal_varlen_fwd(q, k, v, cu_seqlens, max_seqlen: int,
     return out, lse
 
 
-__all__ = ["gqa_causal_fwd", "gqa_causal_varlen_fwd", "status_string", "version", "lds_bytes",
-           "load_library", "H3AttnError", "LIBRARY", "EXPORTED"]
+def splitkv_workspace_bytes(seq_len: int, n_q_heads: int, head_dim: int, num_splits: int) -> int:
+    """Bytes of device workspace :func:`gqa_causal_splitkv_fwd` needs (0 if invalid)."""
+    return int(load_library().h3attn_gqa_causal_splitkv_workspace_bytes(
+        int(seq_len), int(n_q_heads), int(head_dim), int(num_splits)))
+
+
+def gqa_causal_splitkv_fwd(q, k, v, num_splits: int, softmax_scale: float | None = None,
+                           out=None, lse=None, workspace=None, return_lse: bool = True,
+                           stream=None):
+    """Split-KV (two-dispatch) causal GQA forward of one sequence.
+
+    Same inputs and result as :func:`gqa_causal_fwd`; the KV range of every query
+    block is cut into ``num_splits`` parts whose partial results go through
+    ``workspace`` (a contiguous uint8 CUDA tensor of at least
+    :func:`splitkv_workspace_bytes` bytes, 256-byte aligned; allocated here with
+    torch when not given) and are merged by a second kernel.
+    """
+    import torch
+
+    _check_tensors(q, k, v)
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    out, lse = _outputs(q, out, lse, return_lse)
+    lib = load_library()
+    need = int(lib.h3attn_gqa_causal_splitkv_workspace_bytes(S, Hq, D, int(num_splits)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif (not isinstance(workspace, torch.Tensor) or workspace.device != q.device
+          or not workspace.is_contiguous()):
+        raise ValueError("h3attn: workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = lib.h3attn_gqa_causal_splitkv_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, S, Hq, Hkv, D, scale, int(num_splits),
+        workspace.data_ptr(), ws_bytes, _stream_handle(stream, q.device))
+    _check(rc)
+    return out, lse
+
+
+__all__ = ["gqa_causal_fwd", "gqa_causal_varlen_fwd", "gqa_causal_splitkv_fwd",
+           "splitkv_workspace_bytes", "status_string", "version", "lds_bytes", "load_library",
+           "H3AttnError", "LIBRARY", "EXPORTED", "MAX_SPLITS"]

@@ -107,7 +107,18 @@ struct FwdParams {
   int n_qblk;                  // query blocks per sequence = ceil(seq_len / TOK_WG)
   int hq, hkv;
   float scale_log2;            // softmax_scale * log2(e)
+  // split-KV partials (split instances only)
+  float* o_part;               // [num_splits, T, hq, D] fp32, each normalised over its keys
+  float* lse_part;             // [num_splits, hq, T] fp32, -inf where a row has no key
+  int num_splits;
 };
+
+// First KV tile of split `s` of a query block with `n` tiles in `ns` splits: split s
+// covers tiles [split_first_tile(n, s, ns), split_first_tile(n, s + 1, ns)), contiguous
+// ranges of near-equal length (empty when ns > n).
+__host__ __device__ __forceinline__ int split_first_tile(int n, int s, int ns) {
+  return (int)(((long long)n * s) / ns);
+}
 
 // A lane whose weights over one KV tile (32 keys of its row, each exp2 of the
 // score minus the running max) sum to more than this sends its row through
@@ -194,7 +205,10 @@ __device__ __forceinline__ void fill_tile_lds(const uint16_t* ksrc, const uint16
   }
 }
 
-template <class C, bool VARLEN>
+// VARLEN: packed batch (cu_seqlens).  SPLIT: split-KV partials -- the workgroups of a
+// query block each take one contiguous range of its KV tiles and write O and LSE over
+// those keys to o_part / lse_part, for the merge kernel to combine.
+template <class C, bool VARLEN, bool SPLIT = false>
 __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams p) {
   constexpr int D = C::D, G = C::G, BN = C::BN;
   constexpr int NKB = BN / 32;   // 32-key blocks per tile
@@ -218,6 +232,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   int bid = blockIdx.x;
   const int g = bid % p.hkv;
   bid /= p.hkv;
+  int split = 0;
+  if constexpr (SPLIT) {
+    split = bid % p.num_splits;
+    bid /= p.num_splits;
+  }
   const int seq = bid % p.num_seqs;
   bid /= p.num_seqs;
   const int qblk = p.n_qblk - 1 - bid;
@@ -233,7 +252,14 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   }
   const int q0 = qblk * C::TOK_WG;
   if (q0 >= len) return;                              // uniform over the workgroup
-  const int n_tiles = (min(q0 + C::TOK_WG, len) + BN - 1) / BN;
+  // KV tiles [t0, t0 + n_tiles): the block's causal range, or this split's part of it
+  int t0 = 0;
+  int n_tiles = (min(q0 + C::TOK_WG, len) + BN - 1) / BN;
+  if constexpr (SPLIT) {
+    t0 = split_first_tile(n_tiles, split, p.num_splits);
+    n_tiles = split_first_tile(n_tiles, split + 1, p.num_splits) - t0;
+    if (n_tiles == 0) return;                         // uniform over the workgroup
+  }
 
   const int wq0 = q0 + wave * C::TOK_W;               // first token of this wave
   const int w_last = (wq0 < len) ? min(wq0 + C::TOK_W, len) - 1 : -1;
@@ -279,6 +305,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
     fill_off[n] = (unsigned)(row * kv_stride * 2 + logical * 16);
   }
   auto fill_tile = [&](int kt, uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
+    kt += t0;                                         // local tile -> tile of the sequence
     const int rows = min(len - kt * BN, BN);
     const size_t tile0 = (size_t)kt * BN * kv_stride;
     fill_tile_lds<C>(kg + tile0, vg + tile0, rows * kv_stride * 2, kdst, vdst, wave, fill_off);
@@ -358,8 +385,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
     __builtin_amdgcn_sched_group_barrier(0x008, KPF, 0);
   };
 
-  // causal mask and online softmax of tile kt (scores in s) -> pf, l_run, m_run
-  auto softmax = [&](int kt) __attribute__((always_inline)) {
+  // causal mask and online softmax of tile kt of the sequence (scores in s) -> pf, l_run,
+  // m_run; `first`: the first tile this workgroup processes
+  auto softmax = [&](int kt, bool first) __attribute__((always_inline)) {
     // causal mask, only on tiles that reach past the wave's first token
     if (kt * BN + BN - 1 > wq0) {
 #pragma unroll
@@ -396,7 +424,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
     // any tile where some lane's weights sum past WEIGHT_SUM_LIMIT, take the max path.
     float lsum = 0.0f;
     uint64_t flagged = 0;
-    bool max_path = (kt == 0);
+    bool max_path = first;
     if (!max_path) {
       lsum = exponentiate();
       flagged = __builtin_amdgcn_ballot_w64(!(lsum <= WEIGHT_SUM_LIMIT));
@@ -411,7 +439,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = pair_max(mx);
       // rows raised: all on the first tile, else those whose lane or partner lane flagged
-      const bool raise = kt == 0 || (((flagged >> col) | (flagged >> (col + 32))) & 1) != 0;
+      const bool raise = first || (((flagged >> col) | (flagged >> (col + 32))) & 1) != 0;
       const float m_new = raise ? fmaxf(m_run, mx * p.scale_log2) : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
@@ -452,7 +480,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   // group therefore issues MFMAs (P.V then scores) while the other runs its softmax on the
   // VALU, and the SIMD's matrix core and VALU work at the same time.
   const int group = wave / (C::NW / 2);
-  const int t_last = (w_last >= 0) ? w_last / BN : -1;   // last tile with a visible key
+  // last local tile with a key visible to this wave (-1: none in this range)
+  const int t_last = (w_last >= 0) ? min(w_last / BN - t0, n_tiles - 1) : -1;
   auto sync = [&](int j) __attribute__((always_inline)) {
     wait_vmem();        // this wave's share of tile j+1 has landed in LDS ...
     __syncthreads();    // ... and so has every other wave's; b(j) passed
@@ -469,7 +498,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
     if (mine) {
 #pragma unroll
       for (int i = 0; i < VPF; ++i) vf[i] = v_frag(v_lds[ST], i);   // overlap the softmax
-      softmax(t);
+      softmax(t0 + t, t == 0);
     }
     if (group == 0) sync(t);
     if (mine) pv(v_lds[ST]);
@@ -491,6 +520,27 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2
   const float l_tot = pair_sum(l_run);
+  if constexpr (SPLIT) {
+    // partial over this split's keys, fp32; a row that saw no key gets O = 0, LSE = -inf
+    if (my_valid) {
+      const bool empty = !(l_tot > 0.0f);
+      const float inv = empty ? 0.0f : 1.0f / l_tot;
+      float* op = p.o_part + (((size_t)split * p.total_tokens + start + my_tok) * p.hq + my_head) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 x;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) x[t] = acc[db][4 * r4 + t] * inv;
+          *(f32x4*)(op + 32 * db + 8 * r4 + 4 * half) = x;
+        }
+      if (half == 0)
+        p.lse_part[((size_t)split * p.hq + my_head) * p.total_tokens + start + my_tok] =
+            empty ? -__builtin_inff() : (m_run + __builtin_amdgcn_logf(l_tot)) * LN2;
+    }
+    return;
+  }
   if (my_valid) {
     const float inv = 1.0f / l_tot;
     uint16_t* op = p.o + ((size_t)(start + my_tok) * p.hq + my_head) * D;

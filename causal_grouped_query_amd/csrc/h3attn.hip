@@ -15,12 +15,14 @@
 #include <cstring>
 
 #include "gqa_fwd_kernel.hpp"
+#include "gqa_merge_kernel.hpp"
 #include "h3attn.h"
 
 namespace {
 
 using h3attn::FwdConfig;
 using h3attn::FwdParams;
+using h3attn::MergeParams;
 
 constexpr int kWaves = 8;       // waves per workgroup: 2 per SIMD
 constexpr int kKeysPerTile = 64;
@@ -77,6 +79,67 @@ int dispatch(int D, int G, const FwdParams& p, hipStream_t stream) {
     }
   }
   return H3ATTN_ERR_UNSUPPORTED;
+}
+
+// Split-KV: the split instance of the attention kernel writes per-split partials to the
+// workspace, then the merge kernel combines them into o and lse (same stream, in order).
+template <int D, int G>
+int launch_split(FwdParams p, hipStream_t stream) {
+  using C = Cfg<D, G>;
+  p.n_qblk = (p.seq_len + C::TOK_WG - 1) / C::TOK_WG;
+  const long long blocks = (long long)p.n_qblk * p.hkv * p.num_splits;
+  if (blocks == 0) return H3ATTN_OK;
+  if (blocks > 0x7fffffffLL) return H3ATTN_ERR_SHAPE;
+  hipLaunchKernelGGL((h3attn::gqa_causal_fwd_kernel<C, false, true>), dim3((unsigned)blocks),
+                     dim3(C::THREADS), 0, stream, p);
+  if (hipGetLastError() != hipSuccess) return H3ATTN_ERR_LAUNCH;
+  MergeParams m{};
+  m.o_part = p.o_part;
+  m.lse_part = p.lse_part;
+  m.o = p.o;
+  m.lse = p.lse;
+  m.seq_len = p.seq_len;
+  m.hq = p.hq;
+  m.num_splits = p.num_splits;
+  m.tok_wg = C::TOK_WG;
+  m.bn = C::BN;
+  constexpr int rows_per_block = h3attn::MERGE_THREADS / (D / 4);
+  const long long rows = (long long)p.seq_len * p.hq;
+  const long long mblocks = (rows + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL((h3attn::merge_splits_kernel<D>), dim3((unsigned)mblocks),
+                     dim3(h3attn::MERGE_THREADS), 0, stream, m);
+  return hipGetLastError() == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
+}
+
+int dispatch_split(int D, int G, const FwdParams& p, hipStream_t stream) {
+  if (D == 128) {
+    switch (G) {
+      case 1: return launch_split<128, 1>(p, stream);
+      case 2: return launch_split<128, 2>(p, stream);
+      case 4: return launch_split<128, 4>(p, stream);
+      case 8: return launch_split<128, 8>(p, stream);
+    }
+  } else if (D == 64) {
+    switch (G) {
+      case 1: return launch_split<64, 1>(p, stream);
+      case 2: return launch_split<64, 2>(p, stream);
+      case 4: return launch_split<64, 4>(p, stream);
+      case 8: return launch_split<64, 8>(p, stream);
+    }
+  }
+  return H3ATTN_ERR_UNSUPPORTED;
+}
+
+// Workspace layout of the split-KV call: partial O (fp32 [num_splits, S, Hq, D]) at
+// offset 0, partial LSE (fp32 [num_splits, Hq, S]) at the next 256-byte boundary.
+// Returns 0 for invalid sizes.
+size_t split_workspace_layout(long long S, long long Hq, long long D, long long ns,
+                              size_t* lse_offset) {
+  if (S < 0 || Hq <= 0 || D <= 0 || ns < 1 || ns > H3ATTN_MAX_SPLITS) return 0;
+  const size_t o_bytes = (size_t)ns * (size_t)S * (size_t)Hq * (size_t)D * sizeof(float);
+  const size_t lse_off = (o_bytes + 255) / 256 * 256;
+  if (lse_offset) *lse_offset = lse_off;
+  return lse_off + (size_t)ns * (size_t)Hq * (size_t)S * sizeof(float);
 }
 
 // Checks shared by both entry points; returns a status.
@@ -152,24 +215,64 @@ int h3attn_gqa_causal_varlen_fwd(const void* q, const void* k, const void* v, vo
   return dispatch<true>(D, Hq / Hkv, p, static_cast<hipStream_t>(hip_stream));
 }
 
+size_t h3attn_gqa_causal_splitkv_workspace_bytes(int S, int Hq, int D, int num_splits) {
+  return split_workspace_layout(S, Hq, D, num_splits, nullptr);
+}
+
+int h3attn_gqa_causal_splitkv_fwd(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, int S, int Hq, int Hkv, int D,
+                                  float softmax_scale, int num_splits, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream) {
+  const int rc = check_common(q, k, v, o, lse, S, Hq, Hkv, D, softmax_scale);
+  if (rc != H3ATTN_OK) return rc;
+  if (num_splits < 1 || num_splits > H3ATTN_MAX_SPLITS) return H3ATTN_ERR_SHAPE;
+  if (S == 0) return H3ATTN_OK;
+  size_t lse_off = 0;
+  const size_t need = split_workspace_layout(S, Hq, D, num_splits, &lse_off);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      workspace_bytes < need)
+    return H3ATTN_ERR_WORKSPACE;
+  if (!device_ok()) return H3ATTN_ERR_DEVICE;
+  FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.cu_seqlens = nullptr;
+  p.seq_len = S;
+  p.total_tokens = S;
+  p.num_seqs = 1;
+  p.hq = Hq;
+  p.hkv = Hkv;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.o_part = static_cast<float*>(workspace);
+  p.lse_part = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + lse_off);
+  p.num_splits = num_splits;
+  return dispatch_split(D, Hq / Hkv, p, static_cast<hipStream_t>(hip_stream));
+}
+
 const char* h3attn_status_string(int status) {
   switch (status) {
     case H3ATTN_OK: return "ok";
     case H3ATTN_ERR_NULL: return "a required pointer is NULL";
     case H3ATTN_ERR_SHAPE:
       return "invalid shape: negative size, Hq not a multiple of Hkv, inconsistent offsets, "
-             "or tokens*Hq*D >= 2^31";
+             "tokens*Hq*D >= 2^31, or num_splits outside 1..64";
     case H3ATTN_ERR_UNSUPPORTED:
       return "unsupported configuration: head dim must be 64 or 128 and Hq/Hkv 1, 2, 4 or 8";
     case H3ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case H3ATTN_ERR_SCALE: return "softmax_scale must be finite and > 0";
     case H3ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
     case H3ATTN_ERR_DEVICE: return "no usable gfx950 device is current";
+    case H3ATTN_ERR_WORKSPACE:
+      return "workspace is NULL, not 256-byte aligned, or smaller than "
+             "h3attn_gqa_causal_splitkv_workspace_bytes()";
     default: return "unknown status";
   }
 }
 
-int h3attn_version(void) { return 100; }
+int h3attn_version(void) { return 200; }
 
 int h3attn_lds_bytes(int D, int G) {
   if (D == 128) {

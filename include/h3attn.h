@@ -34,6 +34,7 @@
 #ifndef H3ATTN_H
 #define H3ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #if defined(__GNUC__) || defined(__clang__)
@@ -56,8 +57,12 @@ typedef enum {
   H3ATTN_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
   H3ATTN_ERR_SCALE = 5,       /* softmax_scale not finite or not > 0 */
   H3ATTN_ERR_LAUNCH = 6,      /* the HIP kernel launch failed (hipGetLastError) */
-  H3ATTN_ERR_DEVICE = 7       /* no usable gfx950 device is current */
+  H3ATTN_ERR_DEVICE = 7,      /* no usable gfx950 device is current */
+  H3ATTN_ERR_WORKSPACE = 8    /* split-KV workspace NULL, not 256-byte aligned, or too small */
 } h3attn_status;
+
+/* Largest num_splits the split-KV entry point accepts. */
+#define H3ATTN_MAX_SPLITS 64
 
 /*
  * Fixed-length causal GQA forward over one sequence of S tokens.
@@ -99,6 +104,43 @@ H3ATTN_API int h3attn_gqa_causal_varlen_fwd(const void* q, const void* k, const 
                                  const int32_t* cu_seqlens, int num_seqs, int total_tokens,
                                  int max_seqlen, int Hq, int Hkv, int D, float softmax_scale,
                                  void* hip_stream);
+
+/*
+ * Split-KV (multi-dispatch) causal GQA forward over one sequence: the first fix
+ * direction of the issue ("Suggested fix directions": the score computation split
+ * across several dispatches with intermediate results in global memory).
+ *
+ * The query tokens are cut into blocks (32 tokens for G = 8; 256/G in general), and the
+ * causal KV range of each block, ceil(min(block end, S) / 64) tiles of 64 keys, into
+ * num_splits contiguous ranges of near-equal length: split c of a block with n tiles
+ * covers tiles [floor(n*c/num_splits), floor(n*(c+1)/num_splits)).  A first kernel
+ * writes, for every (split, token, head), the attention over that split's keys --
+ * O_c normalised over those keys (fp32) and LSE_c (fp32, -inf when the row saw none)
+ * -- into the workspace; a second kernel, on the same stream, combines them:
+ *     LSE = log(sum_c exp(LSE_c)),   O = sum_c exp(LSE_c - LSE) * O_c   (rounded to bf16).
+ * The result is the same function as h3attn_gqa_causal_fwd; only rounding differs.
+ *
+ *   q, k, v, o, lse, S, Hq, Hkv, D, softmax_scale, hip_stream: as h3attn_gqa_causal_fwd.
+ *   num_splits       1 .. H3ATTN_MAX_SPLITS (else H3ATTN_ERR_SHAPE).
+ *   workspace        DEVICE memory the caller allocated, 256-byte aligned, at least
+ *                    h3attn_gqa_causal_splitkv_workspace_bytes(S, Hq, D, num_splits)
+ *                    bytes (else H3ATTN_ERR_WORKSPACE); contents need no
+ *                    initialisation and are left undefined.  The library allocates
+ *                    nothing.  Two calls in flight must not share a workspace.
+ *   workspace_bytes  its size.
+ * S == 0 is a no-op (pointers may then be NULL).
+ */
+H3ATTN_API int h3attn_gqa_causal_splitkv_fwd(const void* q, const void* k, const void* v,
+                                             void* o, float* lse, int S, int Hq, int Hkv,
+                                             int D, float softmax_scale, int num_splits,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* hip_stream);
+
+/* Workspace bytes h3attn_gqa_causal_splitkv_fwd needs: partial O, fp32
+ * [num_splits, S, Hq, D], then partial LSE, fp32 [num_splits, Hq, S], at the next
+ * 256-byte boundary.  0 for invalid arguments. */
+H3ATTN_API size_t h3attn_gqa_causal_splitkv_workspace_bytes(int S, int Hq, int D,
+                                                            int num_splits);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 H3ATTN_API const char* h3attn_status_string(int status);
