@@ -40,7 +40,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=workloads.PRIMARY, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--workload", default=workloads.PRIMARY,
+                    choices=sorted({**workloads.WORKLOADS, **workloads.SPLITKV_WORKLOADS}))
+    ap.add_argument("--path", default="fused", choices=("fused", "splitkv"),
+                    help="fused: one kernel per call (the default, the benchmarked path); "
+                         "splitkv: per-split partials through a workspace, then a merge kernel")
+    ap.add_argument("--splits", type=int, default=4, help="KV splits of the splitkv path")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target wall time of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -69,14 +74,13 @@ def recorded_traffic():
 
     profiles/gqa_causal_fwd_s10231_hbm_traffic.txt holds a line
     `traffic_bytes_per_launch: N source_sha256: H`; the figure applies only while the
-    kernel sources still hash to H."""
+    attention kernel's source (csrc/gqa_fwd_kernel.hpp, which also fixes its launch
+    configuration) still hashes to H."""
     import hashlib
 
-    src = os.path.join(ROOT, "causal_grouped_query_amd", "csrc")
-    h = hashlib.sha256()
-    for name in sorted(os.listdir(src)):
-        with open(os.path.join(src, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "causal_grouped_query_amd", "csrc", "gqa_fwd_kernel.hpp"),
+              "rb") as f:
+        h = hashlib.sha256(f.read())
     path = os.path.join(ROOT, "profiles", "gqa_causal_fwd_s10231_hbm_traffic.txt")
     try:
         with open(path) as f:
@@ -148,7 +152,10 @@ def main():
 
     import causal_grouped_query_amd as h3
 
-    w = workloads.WORKLOADS[args.workload]
+    w = {**workloads.WORKLOADS, **workloads.SPLITKV_WORKLOADS}[args.workload]
+    if args.path == "splitkv" and w.varlen:
+        print("bench.py: the split-KV path takes one sequence, not a packed batch", file=sys.stderr)
+        sys.exit(2)
     log(f"workload {w.name}: seqlens={w.seqlens} Hq={w.n_q_heads} Hkv={w.n_kv_heads} "
         f"D={w.head_dim}")
     inp = workloads.generate(w)
@@ -157,9 +164,16 @@ def main():
     lse = torch.empty((w.n_q_heads, w.total_tokens), dtype=torch.float32, device="cuda")
     cu = torch.tensor(w.cu_seqlens, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
+    workspace = None
+    if args.path == "splitkv":
+        need = h3.splitkv_workspace_bytes(w.total_tokens, w.n_q_heads, w.head_dim, args.splits)
+        workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
 
     def step():
-        if w.varlen:
+        if args.path == "splitkv":
+            h3.gqa_causal_splitkv_fwd(q, k, v, args.splits, softmax_scale=w.scale, out=o, lse=lse,
+                                      workspace=workspace, stream=stream)
+        elif w.varlen:
             h3.gqa_causal_varlen_fwd(q, k, v, cu, max(w.seqlens), softmax_scale=w.scale, out=o,
                                      lse=lse, stream=stream)
         else:
@@ -213,6 +227,8 @@ def main():
             "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim,
             "causal": True,
+            "path": args.path,
+            **({"splits": args.splits} if args.path == "splitkv" else {}),
             "inputs": ("N(0,1) bf16, seeded" if w.kind == "normal" else
                        "stress: 4 N(0,1) Q/K, U(-1,1) V, 5% shared spike keys, seeded"),
         },
@@ -223,8 +239,10 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": recorded_traffic() if w.name == workloads.PRIMARY else None,
-            "kernel": "gqa_causal_fwd_kernel",
+            "traffic": (recorded_traffic() if w.name == workloads.PRIMARY and args.path == "fused"
+                        else None),
+            "kernel": ("gqa_causal_fwd_kernel" if args.path == "fused" else
+                       "gqa_causal_fwd_kernel<split> + merge_splits_kernel (one call, timed together)"),
             "avg_launch_ms": round(avg_launch_ms, 5),
             "algorithmic_flop_per_launch": flop,
         },

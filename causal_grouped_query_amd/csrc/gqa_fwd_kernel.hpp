@@ -149,6 +149,11 @@ struct FwdConfig {
   static_assert(TILE_PIECES % NW == 0 && PIECES_PER_WAVE >= 1, "tile fill divides over waves");
 };
 
+// The instance the library launches for head dim D and group size G: 8 waves per
+// workgroup (2 per SIMD, one workgroup per CU), 64 keys per KV tile.
+template <int D, int G>
+using LaunchConfig = FwdConfig<D, G, 8, 64>;
+
 // Physical 16-byte chunk of logical chunk `chunk` in LDS row `key` (the gfx950 LDS has
 // 64 four-byte banks: one 256-byte bank row).  The XOR term is chosen so that
 //   * 16-byte reads of one logical chunk down 16 consecutive keys (the K operand: 16

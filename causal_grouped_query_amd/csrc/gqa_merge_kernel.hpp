@@ -58,20 +58,41 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_splits_kernel(MergeParams
   const int n = (min(q0 + p.tok_wg, p.seq_len) + p.bn - 1) / p.bn;
   const int ns = p.num_splits;
 
+  auto holds_tiles = [&](int c) {
+    return split_first_tile(n, c, ns) < split_first_tile(n, c + 1, ns);
+  };
   float m = -__builtin_inff();
+  int c_last = 0;                                     // a split with tiles (the last one)
   for (int c = 0; c < ns; ++c)
-    if (split_first_tile(n, c, ns) < split_first_tile(n, c + 1, ns))
+    if (holds_tiles(c)) {
       m = fmaxf(m, p.lse_part[((size_t)c * p.hq + head) * p.seq_len + token]);
+      c_last = c;
+    }
 
+  // Four splits per step, all loads issued before any is used (memory-level parallelism).
+  // A slot past num_splits or on a split without tiles reads the c_last split's data
+  // (finite, in bounds) and gets weight 0.
   float wsum = 0.0f;
   f32x4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int c = 0; c < ns; ++c) {
-    if (!(split_first_tile(n, c, ns) < split_first_tile(n, c + 1, ns))) continue;
-    const float lc = p.lse_part[((size_t)c * p.hq + head) * p.seq_len + token];
-    const float w = __builtin_amdgcn_exp2f((lc - m) * LOG2E);   // 0 for a split with no key
-    const f32x4v oc = *(const f32x4v*)(p.o_part + (((size_t)c * p.seq_len + token) * p.hq + head) * D + d0);
-    wsum += w;
-    acc += w * oc;
+  for (int c0 = 0; c0 < ns; c0 += 4) {
+    f32x4v oc[4];
+    float lc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u;
+      const bool ok = c < ns && holds_tiles(c);
+      const int cc = ok ? c : c_last;
+      lc[u] = p.lse_part[((size_t)cc * p.hq + head) * p.seq_len + token];
+      oc[u] = *(const f32x4v*)(p.o_part +
+                               (((size_t)cc * p.seq_len + token) * p.hq + head) * D + d0);
+      lc[u] = ok ? lc[u] : -__builtin_inff();
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = __builtin_amdgcn_exp2f((lc[u] - m) * LOG2E);   // 0 for -inf
+      wsum += w;
+      acc += w * oc[u];
+    }
   }
   const float inv = 1.0f / wsum;
   const bf16x4v y = __builtin_convertvector(acc * inv, bf16x4v);

@@ -24,11 +24,8 @@ using h3attn::FwdConfig;
 using h3attn::FwdParams;
 using h3attn::MergeParams;
 
-constexpr int kWaves = 8;       // waves per workgroup: 2 per SIMD
-constexpr int kKeysPerTile = 64;
-
 template <int D, int G>
-using Cfg = FwdConfig<D, G, kWaves, kKeysPerTile>;
+using Cfg = h3attn::LaunchConfig<D, G>;
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other

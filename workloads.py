@@ -119,6 +119,17 @@ WORKLOADS = {
     )
 }
 
+# Shapes for the split-KV path only (not the pages' workloads): with a single KV head the
+# single-dispatch kernel has one workgroup per query block, 128 at S=4096, too few for
+# 256 compute units; splitting each block's KV range multiplies the workgroups.
+SPLITKV_WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("few_heads_s4096_h8kv1", (4096,), 8, 1, 128, seed=6,
+                 note="one KV head: too few query blocks to fill the GPU without splits"),
+    )
+}
+
 PRIMARY = "failing_s10231"
 
 
