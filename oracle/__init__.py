@@ -75,6 +75,10 @@ class Oracle:
                                                    ctypes.c_float, i64, i64, p_i64, i64, p_f64,
                                                    p_f64, ctypes.c_int]
         lib.oracle_gqa_causal_keyrange.restype = ctypes.c_int
+        lib.oracle_gqa_bidirectional.argtypes = [p_u16, p_u16, p_u16, i64, i64, i64, i64,
+                                                 ctypes.c_float, p_i64, i64, p_f64, p_f64,
+                                                 ctypes.c_int]
+        lib.oracle_gqa_bidirectional.restype = ctypes.c_int
         lib.oracle_threads.argtypes = [ctypes.c_int]
         lib.oracle_threads.restype = ctypes.c_int
         self._lib = lib
@@ -126,6 +130,36 @@ class Oracle:
         """One sequence: q [S,Hq,D], k/v [S,Hkv,D] bf16 bits -> (o, lse)."""
         return self.gqa_causal_varlen(q, k, v, [0, int(q.shape[0])], scale, tokens=tokens,
                                       threads=threads)
+
+    def gqa_bidirectional(self, q, k, v, scale: float, tokens=None, threads: int = 0):
+        """One sequence, no causal mask: every query sees all S keys -> (o, lse)."""
+        q = _as_bits(q, "q")
+        k = _as_bits(k, "k")
+        v = _as_bits(v, "v")
+        if q.ndim != 3 or k.ndim != 3 or v.shape != k.shape or k.shape[0] != q.shape[0] \
+                or k.shape[2] != q.shape[2]:
+            raise ValueError("oracle: q must be [S,Hq,D] and k, v [S,Hkv,D]")
+        S, Hq, D = q.shape
+        Hkv = k.shape[1]
+        if tokens is None:
+            tokens = np.arange(S, dtype=np.int64)
+        tokens = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64).reshape(-1))
+        n = tokens.size
+        o = np.empty((n, Hq, D), dtype=np.float64)
+        lse = np.empty((Hq, n), dtype=np.float64)
+        if n == 0:
+            return o, lse
+
+        def ptr(a, t):
+            return a.ctypes.data_as(ctypes.POINTER(t))
+
+        rc = self._lib.oracle_gqa_bidirectional(
+            ptr(q, ctypes.c_uint16), ptr(k, ctypes.c_uint16), ptr(v, ctypes.c_uint16), S, Hq,
+            Hkv, D, float(np.float32(scale)), ptr(tokens, ctypes.c_int64), n,
+            ptr(o, ctypes.c_double), ptr(lse, ctypes.c_double), int(threads))
+        if rc != 0:
+            raise ValueError(f"oracle: invalid arguments (code {rc})")
+        return o, lse
 
     def gqa_causal_keyrange(self, q, k, v, scale: float, key_begin: int, key_end: int,
                             tokens=None, threads: int = 0):
@@ -194,6 +228,11 @@ def gqa_causal_keyrange(q, k, v, scale: float, key_begin: int, key_end: int, tok
     """Attention over a key range; see :meth:`Oracle.gqa_causal_keyrange`."""
     return default().gqa_causal_keyrange(q, k, v, scale, key_begin, key_end, tokens=tokens,
                                          threads=threads)
+
+
+def gqa_bidirectional(q, k, v, scale: float, tokens=None, threads: int = 0):
+    """Non-causal GQA in fp64; see :meth:`Oracle.gqa_bidirectional`."""
+    return default().gqa_bidirectional(q, k, v, scale, tokens=tokens, threads=threads)
 
 
 def merge_partials(o_parts, lse_parts):

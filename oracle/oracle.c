@@ -38,6 +38,10 @@
  * O = 0 and LSE = -inf where that set is empty.  Merging partials is done in
  * oracle/__init__.py (merge_partials), in double precision with numpy.
  *
+ * The DiT's attention on the vpipe page and in the h3.c project README is the
+ * same softmax without the causal mask: oracle_gqa_bidirectional lets every
+ * query of a sequence see all S keys (j = 0 .. S-1), nothing else changes.
+ *
  * Parallelism: (token, head) items are independent; OpenMP spreads them over
  * threads.  This changes no arithmetic: each item's sums run in the same order
  * whatever the thread count.
@@ -222,6 +226,53 @@ int oracle_gqa_causal_keyrange(const uint16_t* q, const uint16_t* k, const uint1
       }
       lse_out[h * ntok + ti] = attend_one_row(q + (pos * Hq + h) * D, k, v, Hkv * D, g, D,
                                               scale, first, last, scores, o_row);
+    }
+    free(scores);
+  }
+  return status;
+}
+
+/*
+ * Bidirectional (non-causal) form, one sequence of S tokens: every query token
+ * attends to all S keys.  Same layouts and return codes as above.
+ */
+int oracle_gqa_bidirectional(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             int64_t S, int64_t Hq, int64_t Hkv, int64_t D, float scale_f32,
+                             const int64_t* tokens, int64_t ntok,
+                             double* o_out, double* lse_out, int threads) {
+  if (!q || !k || !v || !o_out || !lse_out || (ntok > 0 && !tokens)) return -1;
+  if (S < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv != 0) return -2;
+  for (int64_t t = 0; t < ntok; ++t)
+    if (tokens[t] < 0 || tokens[t] >= S) return -4;
+
+  const int64_t G = Hq / Hkv;
+  const double scale = (double)scale_f32;
+  const int64_t n_items = ntok * Hq;
+  int status = 0;
+
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+
+#pragma omp parallel
+  {
+    double* scores = (double*)malloc(sizeof(double) * (size_t)S);
+    if (!scores) {
+#pragma omp atomic write
+      status = -5;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t item = 0; item < n_items; ++item) {
+      if (!scores) continue;
+      const int64_t ti = item / Hq;
+      const int64_t h = item % Hq;
+      const int64_t pos = tokens[ti];
+      const int64_t g = h / G;
+      lse_out[h * ntok + ti] = attend_one_row(q + (pos * Hq + h) * D, k, v, Hkv * D, g, D,
+                                              scale, 0, S - 1, scores,
+                                              o_out + (ti * Hq + h) * D);
     }
     free(scores);
   }

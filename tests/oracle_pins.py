@@ -17,7 +17,10 @@ Each ``pin_*`` function takes an :class:`oracle.Oracle` and raises
   enough to overflow exp() without the max shift,
 * for the split-KV building blocks: attention over a key range against dense
   masked matrices, a one-key range in closed form, and the merge of partials
-  over a partition of the keys against the full result.
+  over a partition of the keys against the full result,
+* for the bidirectional (non-causal) form: dense matrices, torch's float64
+  SDPA without the causal flag, Q = 0 (mean of all values, LSE = ln S), and
+  invariance under a permutation of the key/value rows.
 
 ``tests/test_oracle_pins.py`` runs them on the real oracle and
 ``tests/test_oracle_mutations.py`` checks that each planted mistake in a copy
@@ -337,6 +340,67 @@ def pin_keyrange_single_key(orc):
             assert abs(lse[h, i] - exact) <= 1e-14 * max(1.0, abs(exact)), (i, h)
 
 
+def pin_bidirectional_brute_force(orc):
+    """No causal mask: dense float64 matrices per head on tiny shapes."""
+    cases = [(1, 2, 1, 8, 300, 1.0), (17, 4, 2, 16, 301, 2.0), (64, 8, 1, 64, 302, 1.0),
+             (45, 4, 4, 32, 303, 4.0)]
+    for S, Hq, Hkv, D, seed, sigma in cases:
+        q, k, v = normal_inputs(seed, S, Hq, Hkv, D, sigma=sigma)
+        scale = default_scale(D)
+        o, lse = orc.gqa_bidirectional(q, k, v, scale)
+        Q, K, V = _f64(q), _f64(k), _f64(v)
+        G = Hq // Hkv
+        for h in range(Hq):
+            g = h // G
+            X = float(np.float32(scale)) * (Q[:, h, :] @ K[:, g, :].T)
+            m = X.max(axis=1, keepdims=True)
+            W = np.exp(X - m)
+            assert np.allclose(lse[h], (m[:, 0] + np.log(W.sum(axis=1))), rtol=1e-13, atol=1e-12)
+            assert np.allclose(o[:, h, :], (W / W.sum(axis=1, keepdims=True)) @ V[:, g, :],
+                               rtol=1e-12, atol=1e-13)
+
+
+def pin_bidirectional_torch_sdpa(orc):
+    """torch float64 scaled_dot_product_attention(is_causal=False), K/V repeated per group."""
+    import torch
+
+    S, Hq, Hkv, D = 50, 8, 2, 32
+    q, k, v = normal_inputs(310, S, Hq, Hkv, D)
+    scale = default_scale(D)
+    o, _ = orc.gqa_bidirectional(q, k, v, scale)
+    Q, K, V = (torch.from_numpy(_f64(x)).permute(1, 0, 2) for x in (q, k, v))
+    K = K.repeat_interleave(Hq // Hkv, dim=0)
+    V = V.repeat_interleave(Hq // Hkv, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        Q, K, V, is_causal=False, scale=float(np.float32(scale))).permute(1, 0, 2).numpy()
+    assert np.allclose(o, ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_bidirectional_zero_query(orc):
+    """Q = 0: every row is the mean of all S value rows and LSE = ln S."""
+    S, Hq, Hkv, D = 37, 4, 2, 16
+    _, k, v = normal_inputs(320, S, Hq, Hkv, D)
+    q = np.zeros((S, Hq, D), dtype=np.uint16)
+    o, lse = orc.gqa_bidirectional(q, k, v, 0.25)
+    V = _f64(v)
+    for h in range(Hq):
+        assert np.allclose(o[:, h, :], V[:, h // 2, :].mean(axis=0), rtol=0, atol=1e-14)
+    assert np.allclose(lse, np.log(S), rtol=0, atol=1e-14)
+
+
+def pin_bidirectional_key_permutation(orc):
+    """Without a mask the keys form a set: permuting the K/V rows (the same permutation for
+    both) changes O and LSE only by summation-order rounding."""
+    S, Hq, Hkv, D = 60, 4, 2, 32
+    q, k, v = normal_inputs(330, S, Hq, Hkv, D, sigma=2.0)
+    scale = default_scale(D)
+    o, lse = orc.gqa_bidirectional(q, k, v, scale)
+    perm = np.random.Generator(np.random.PCG64(331)).permutation(S)
+    o2, lse2 = orc.gqa_bidirectional(q, k[perm], v[perm], scale)
+    assert np.allclose(o, o2, rtol=1e-12, atol=1e-13)
+    assert np.allclose(lse, lse2, rtol=1e-13, atol=1e-12)
+
+
 ALL_PINS = [
     pin_brute_force_dense,
     pin_torch_sdpa_float64,
@@ -352,4 +416,8 @@ ALL_PINS = [
     pin_keyrange_brute_force,
     pin_merge_of_key_partition,
     pin_keyrange_single_key,
+    pin_bidirectional_brute_force,
+    pin_bidirectional_torch_sdpa,
+    pin_bidirectional_zero_query,
+    pin_bidirectional_key_permutation,
 ]

@@ -34,6 +34,8 @@ MUTANTS = {
                                "const int64_t first = 0;"),
     "keyrange_empty_lse_zero": ("lse_out[h * ntok + ti] = -INFINITY;",
                                 "lse_out[h * ntok + ti] = 0.0;"),
+    "bidirectional_masked": ("scale, 0, S - 1, scores,", "scale, 0, pos, scores,"),
+    "bidirectional_misses_last_key": ("scale, 0, S - 1, scores,", "scale, 0, S - 2 + (S == 1), scores,"),
 }
 
 
