@@ -41,11 +41,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=workloads.PRIMARY,
-                    choices=sorted({**workloads.WORKLOADS, **workloads.SPLITKV_WORKLOADS}))
+                    choices=sorted(workloads.ALL_WORKLOADS))
     ap.add_argument("--path", default="fused", choices=("fused", "splitkv"),
                     help="fused: one kernel per call (the default, the benchmarked path); "
                          "splitkv: per-split partials through a workspace, then a merge kernel")
     ap.add_argument("--splits", type=int, default=4, help="KV splits of the splitkv path")
+    ap.add_argument("--head-major", action="store_true",
+                    help="bidirectional workloads: write O as [Hq, S, D]")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target wall time of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -98,6 +100,14 @@ def to_device(bits, torch):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+def reference(oracle, inp, w, tokens):
+    """The oracle's (O, LSE) for the sampled query tokens of workload w."""
+    if not w.causal:
+        return oracle.gqa_bidirectional(inp["q"], inp["k"], inp["v"], w.scale, tokens=tokens)
+    return oracle.gqa_causal_varlen(inp["q"], inp["k"], inp["v"], w.cu_seqlens, w.scale,
+                                    tokens=tokens)
+
+
 def cpu_baseline(inp, w, target_s: float):
     """fp64 oracle throughput on a bounded sample of query tokens (all heads)."""
     import oracle
@@ -107,20 +117,22 @@ def cpu_baseline(inp, w, target_s: float):
     starts = np.concatenate([[0], np.cumsum(w.seqlens)[:-1]])
 
     def pair_count(tokens):
-        # visible keys of each packed token = its local position + 1
+        # visible keys of each packed token: its local position + 1 (all S keys without
+        # the causal mask)
+        if not w.causal:
+            return int(len(tokens) * T)
         seq = np.searchsorted(np.cumsum(w.seqlens), tokens, side="right")
         return int(np.sum(tokens - starts[seq] + 1))
 
     def run(tokens):
         t0 = time.perf_counter()
-        oracle.gqa_causal_varlen(inp["q"], inp["k"], inp["v"], w.cu_seqlens, w.scale,
-                                 tokens=tokens)
+        reference(oracle, inp, w, tokens)
         return time.perf_counter() - t0
 
     calib = rng.integers(0, T, size=4)
     dt = run(calib)
     rate = 4 * w.head_dim * w.n_q_heads * pair_count(calib) / max(dt, 1e-6)   # flop/s
-    per_token = 4 * w.head_dim * w.n_q_heads * (T / len(w.seqlens)) / 2
+    per_token = 4 * w.head_dim * w.n_q_heads * (T / len(w.seqlens)) / (2 if w.causal else 1)
     n = int(np.clip(target_s * rate / per_token, 8, T))
     tokens = np.sort(rng.integers(0, T, size=n))
     log(f"cpu baseline: {n} sampled query tokens x {w.n_q_heads} heads "
@@ -133,7 +145,8 @@ def cpu_baseline(inp, w, target_s: float):
         "cores": oracle.threads(),
         "kind": "oracle",
         "sample": (f"{n} query tokens drawn uniformly from the {w.name} workload, all "
-                   f"{w.n_q_heads} heads, full causal rows; {flop:.3e} flop in {dt:.1f} s"),
+                   f"{w.n_q_heads} heads, full {'causal ' if w.causal else ''}rows; "
+                   f"{flop:.3e} flop in {dt:.1f} s"),
     }
 
 
@@ -152,15 +165,16 @@ def main():
 
     import causal_grouped_query_amd as h3
 
-    w = {**workloads.WORKLOADS, **workloads.SPLITKV_WORKLOADS}[args.workload]
-    if args.path == "splitkv" and w.varlen:
-        print("bench.py: the split-KV path takes one sequence, not a packed batch", file=sys.stderr)
+    w = workloads.ALL_WORKLOADS[args.workload]
+    if args.path == "splitkv" and (w.varlen or not w.causal):
+        print("bench.py: the split-KV path takes one causal sequence", file=sys.stderr)
         sys.exit(2)
     log(f"workload {w.name}: seqlens={w.seqlens} Hq={w.n_q_heads} Hkv={w.n_kv_heads} "
         f"D={w.head_dim}")
     inp = workloads.generate(w)
     q, k, v = to_device(inp["q"], torch), to_device(inp["k"], torch), to_device(inp["v"], torch)
-    o = torch.empty_like(q)
+    o = (torch.empty((w.n_q_heads, w.total_tokens, w.head_dim), dtype=torch.bfloat16,
+                     device="cuda") if args.head_major else torch.empty_like(q))
     lse = torch.empty((w.n_q_heads, w.total_tokens), dtype=torch.float32, device="cuda")
     cu = torch.tensor(w.cu_seqlens, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -173,6 +187,9 @@ def main():
         if args.path == "splitkv":
             h3.gqa_causal_splitkv_fwd(q, k, v, args.splits, softmax_scale=w.scale, out=o, lse=lse,
                                       workspace=workspace, stream=stream)
+        elif not w.causal:
+            h3.gqa_fwd(q, k, v, causal=False, head_major_out=args.head_major,
+                       softmax_scale=w.scale, out=o, lse=lse, stream=stream)
         elif w.varlen:
             h3.gqa_causal_varlen_fwd(q, k, v, cu, max(w.seqlens), softmax_scale=w.scale, out=o,
                                      lse=lse, stream=stream)
@@ -201,7 +218,7 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (wall {wall * 1e3 / args.steps:.4f}"
         f" ms/step), launch median {np.median(per_launch):.4f} ms min {per_launch.min():.4f} ms")
 
-    flop = w.causal_flop()
+    flop = w.flop()
     value = flop / (ms_per_step * 1e-3) / 1e12
     avg_launch_ms = float(per_launch.mean())
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
@@ -226,7 +243,8 @@ def main():
             "n_q_heads": w.n_q_heads,
             "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim,
-            "causal": True,
+            "causal": w.causal,
+            **({"o_layout": "[Hq,S,D]"} if args.head_major else {}),
             "path": args.path,
             **({"splits": args.splits} if args.path == "splitkv" else {}),
             "inputs": ("N(0,1) bf16, seeded" if w.kind == "normal" else
@@ -252,10 +270,10 @@ def main():
         import oracle
 
         tokens = workloads.sample_tokens(w.seqlens, 16, seed=w.seed + 1000)
-        o_ref, lse_ref = oracle.gqa_causal_varlen(inp["q"], inp["k"], inp["v"], w.cu_seqlens,
-                                                  w.scale, tokens=tokens)
+        o_ref, lse_ref = reference(oracle, inp, w, tokens)
         idx = torch.from_numpy(tokens).cuda()
-        o_s = o.index_select(0, idx).double().cpu().numpy()
+        o_tok = o.transpose(0, 1) if args.head_major else o      # [T, Hq, D] view
+        o_s = o_tok.index_select(0, idx).double().cpu().numpy()
         l_s = lse.index_select(1, idx).double().cpu().numpy()
         rel = float(np.linalg.norm(o_s - o_ref) / np.linalg.norm(o_ref))
         mx = float(np.abs(o_s - o_ref).max())

@@ -30,7 +30,9 @@ LIBRARY = os.path.join(PKG_DIR, "libh3attn.so")
  ERR_WORKSPACE) = range(9)
 MAX_SPLITS = 64
 
-EXPORTED = ("h3attn_gqa_causal_fwd", "h3attn_gqa_causal_varlen_fwd",
+NONCAUSAL, O_HEAD_MAJOR = 1, 2   # flags of h3attn_gqa_fwd
+
+EXPORTED = ("h3attn_gqa_causal_fwd", "h3attn_gqa_fwd", "h3attn_gqa_causal_varlen_fwd",
             "h3attn_gqa_causal_splitkv_fwd", "h3attn_gqa_causal_splitkv_workspace_bytes",
             "h3attn_status_string", "h3attn_version", "h3attn_lds_bytes")
 
@@ -68,6 +70,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         lib.h3attn_gqa_causal_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                                      i32, i32, f32, vp]
         lib.h3attn_gqa_causal_varlen_fwd.restype = i32
+        lib.h3attn_gqa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
+        lib.h3attn_gqa_fwd.restype = i32
         sz = ctypes.c_size_t
         lib.h3attn_gqa_causal_splitkv_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                                       f32, i32, vp, sz, vp]
@@ -168,6 +172,39 @@ def gqa_causal_fwd(q, k, v, softmax_scale: float | None = None, out=None, lse=No
     return out, lse
 
 
+def gqa_fwd(q, k, v, causal: bool = True, head_major_out: bool = False,
+            softmax_scale: float | None = None, out=None, lse=None, return_lse: bool = True,
+            stream=None):
+    """GQA forward of one sequence with options (h3attn_gqa_fwd).
+
+    ``causal=False`` is the bidirectional form (every query sees all keys);
+    ``head_major_out=True`` returns o as [Hq, S, D] instead of [S, Hq, D].
+    lse is [Hq, S] either way.
+    """
+    import torch
+
+    _check_tensors(q, k, v)
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if head_major_out:
+        if out is None:
+            out = torch.empty((Hq, S, D), dtype=torch.bfloat16, device=q.device)
+        elif out.shape != (Hq, S, D) or out.dtype != torch.bfloat16 or not out.is_contiguous() \
+                or out.device != q.device:
+            raise ValueError("h3attn: out must be a contiguous bf16 tensor [Hq, S, D]")
+        _, lse = _outputs(q, None, lse, return_lse)
+    else:
+        out, lse = _outputs(q, out, lse, return_lse)
+    flags = (0 if causal else NONCAUSAL) | (O_HEAD_MAJOR if head_major_out else 0)
+    lib = load_library()
+    rc = lib.h3attn_gqa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr() if lse is not None else None, S, Hq, Hkv, D, scale,
+                            flags, _stream_handle(stream, q.device))
+    _check(rc)
+    return out, lse
+
+
 def gqa_causal_varlen_fwd(q, k, v, cu_seqlens, max_seqlen: int,
                           softmax_scale: float | None = None, out=None, lse=None,
                           return_lse: bool = True, stream=None):
@@ -239,6 +276,6 @@ def gqa_causal_splitkv_fwd(q, k, v, num_splits: int, softmax_scale: float | None
     return out, lse
 
 
-__all__ = ["gqa_causal_fwd", "gqa_causal_varlen_fwd", "gqa_causal_splitkv_fwd",
+__all__ = ["gqa_causal_fwd", "gqa_fwd", "gqa_causal_varlen_fwd", "gqa_causal_splitkv_fwd",
            "splitkv_workspace_bytes", "status_string", "version", "lds_bytes", "load_library",
-           "H3AttnError", "LIBRARY", "EXPORTED", "MAX_SPLITS"]
+           "H3AttnError", "LIBRARY", "EXPORTED", "MAX_SPLITS", "NONCAUSAL", "O_HEAD_MAJOR"]

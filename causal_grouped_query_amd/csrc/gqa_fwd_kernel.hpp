@@ -49,6 +49,10 @@
 //    The final O = acc / l and LSE use the same max, so the result is the
 //    same function whatever the max; only rounding differs.
 //
+//  * The same kernel also runs without the causal mask (the DiT's attention on
+//    the vpipe page and in the h3.c project README): every block then walks
+//    all KV tiles and only keys past the sequence end are masked.
+//
 //  * Causality: KV tiles past the workgroup's last token are never loaded;
 //    only tiles that reach past a wave's first token apply the elementwise
 //    mask (key > token -> -inf).  Keys past the sequence end are zero-filled
@@ -111,6 +115,7 @@ struct FwdParams {
   float* o_part;               // [num_splits, T, hq, D] fp32, each normalised over its keys
   float* lse_part;             // [num_splits, hq, T] fp32, -inf where a row has no key
   int num_splits;
+  int o_head_major;            // 0: o is [T, hq, D]; 1: o is [hq, T, D]
 };
 
 // First KV tile of split `s` of a query block with `n` tiles in `ns` splits: split s
@@ -212,8 +217,10 @@ __device__ __forceinline__ void fill_tile_lds(const uint16_t* ksrc, const uint16
 
 // VARLEN: packed batch (cu_seqlens).  SPLIT: split-KV partials -- the workgroups of a
 // query block each take one contiguous range of its KV tiles and write O and LSE over
-// those keys to o_part / lse_part, for the merge kernel to combine.
-template <class C, bool VARLEN, bool SPLIT = false>
+// those keys to o_part / lse_part, for the merge kernel to combine.  CAUSAL = false: the
+// bidirectional form, every query sees all keys of its sequence (only keys past the end
+// of the sequence are masked).
+template <class C, bool VARLEN, bool SPLIT = false, bool CAUSAL = true>
 __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams p) {
   constexpr int D = C::D, G = C::G, BN = C::BN;
   constexpr int NKB = BN / 32;   // 32-key blocks per tile
@@ -259,7 +266,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   if (q0 >= len) return;                              // uniform over the workgroup
   // KV tiles [t0, t0 + n_tiles): the block's causal range, or this split's part of it
   int t0 = 0;
-  int n_tiles = (min(q0 + C::TOK_WG, len) + BN - 1) / BN;
+  int n_tiles = ((CAUSAL ? min(q0 + C::TOK_WG, len) : len) + BN - 1) / BN;
   if constexpr (SPLIT) {
     t0 = split_first_tile(n_tiles, split, p.num_splits);
     n_tiles = split_first_tile(n_tiles, split + 1, p.num_splits) - t0;
@@ -393,15 +400,28 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   // causal mask and online softmax of tile kt of the sequence (scores in s) -> pf, l_run,
   // m_run; `first`: the first tile this workgroup processes
   auto softmax = [&](int kt, bool first) __attribute__((always_inline)) {
-    // causal mask, only on tiles that reach past the wave's first token
-    if (kt * BN + BN - 1 > wq0) {
+    if constexpr (CAUSAL) {
+      // causal mask, only on tiles that reach past the wave's first token
+      if (kt * BN + BN - 1 > wq0) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = kt * BN + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (j > my_tok) s[kb][r] = -__builtin_inff();
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int j = kt * BN + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (j > my_tok) s[kb][r] = -__builtin_inff();
+          }
+      }
+    } else {
+      // bidirectional: only the keys past the sequence end (zero-filled in LDS) are masked
+      if (kt * BN + BN > len) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = kt * BN + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (j >= len) s[kb][r] = -__builtin_inff();
+          }
+      }
     }
 
     // P = exp2(S * scale*log2e - m_run) as bf16 and this lane's fp32 sum of the weights
@@ -486,7 +506,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   // VALU, and the SIMD's matrix core and VALU work at the same time.
   const int group = wave / (C::NW / 2);
   // last local tile with a key visible to this wave (-1: none in this range)
-  const int t_last = (w_last >= 0) ? min(w_last / BN - t0, n_tiles - 1) : -1;
+  const int t_last = (w_last < 0)   ? -1
+                     : CAUSAL       ? min(w_last / BN - t0, n_tiles - 1)
+                                    : n_tiles - 1;
   auto sync = [&](int j) __attribute__((always_inline)) {
     wait_vmem();        // this wave's share of tile j+1 has landed in LDS ...
     __syncthreads();    // ... and so has every other wave's; b(j) passed
@@ -548,7 +570,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   }
   if (my_valid) {
     const float inv = 1.0f / l_tot;
-    uint16_t* op = p.o + ((size_t)(start + my_tok) * p.hq + my_head) * D;
+    uint16_t* op = p.o + (p.o_head_major
+                              ? ((size_t)my_head * p.total_tokens + start + my_tok) * D
+                              : ((size_t)(start + my_tok) * p.hq + my_head) * D);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll

@@ -46,33 +46,33 @@ bool device_ok() {
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-template <int D, int G, bool VARLEN>
+template <int D, int G, bool VARLEN, bool CAUSAL>
 int launch(FwdParams p, hipStream_t stream) {
   using C = Cfg<D, G>;
   p.n_qblk = (p.seq_len + C::TOK_WG - 1) / C::TOK_WG;
   const long long blocks = (long long)p.n_qblk * p.hkv * p.num_seqs;
   if (blocks == 0) return H3ATTN_OK;
   if (blocks > 0x7fffffffLL) return H3ATTN_ERR_SHAPE;
-  hipLaunchKernelGGL((h3attn::gqa_causal_fwd_kernel<C, VARLEN>), dim3((unsigned)blocks),
-                     dim3(C::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((h3attn::gqa_causal_fwd_kernel<C, VARLEN, false, CAUSAL>),
+                     dim3((unsigned)blocks), dim3(C::THREADS), 0, stream, p);
   return hipGetLastError() == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
 }
 
-template <bool VARLEN>
+template <bool VARLEN, bool CAUSAL = true>
 int dispatch(int D, int G, const FwdParams& p, hipStream_t stream) {
   if (D == 128) {
     switch (G) {
-      case 1: return launch<128, 1, VARLEN>(p, stream);
-      case 2: return launch<128, 2, VARLEN>(p, stream);
-      case 4: return launch<128, 4, VARLEN>(p, stream);
-      case 8: return launch<128, 8, VARLEN>(p, stream);
+      case 1: return launch<128, 1, VARLEN, CAUSAL>(p, stream);
+      case 2: return launch<128, 2, VARLEN, CAUSAL>(p, stream);
+      case 4: return launch<128, 4, VARLEN, CAUSAL>(p, stream);
+      case 8: return launch<128, 8, VARLEN, CAUSAL>(p, stream);
     }
   } else if (D == 64) {
     switch (G) {
-      case 1: return launch<64, 1, VARLEN>(p, stream);
-      case 2: return launch<64, 2, VARLEN>(p, stream);
-      case 4: return launch<64, 4, VARLEN>(p, stream);
-      case 8: return launch<64, 8, VARLEN>(p, stream);
+      case 1: return launch<64, 1, VARLEN, CAUSAL>(p, stream);
+      case 2: return launch<64, 2, VARLEN, CAUSAL>(p, stream);
+      case 4: return launch<64, 4, VARLEN, CAUSAL>(p, stream);
+      case 8: return launch<64, 8, VARLEN, CAUSAL>(p, stream);
     }
   }
   return H3ATTN_ERR_UNSUPPORTED;
@@ -212,6 +212,32 @@ int h3attn_gqa_causal_varlen_fwd(const void* q, const void* k, const void* v, vo
   return dispatch<true>(D, Hq / Hkv, p, static_cast<hipStream_t>(hip_stream));
 }
 
+int h3attn_gqa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int S,
+                   int Hq, int Hkv, int D, float softmax_scale, int flags, void* hip_stream) {
+  const int rc = check_common(q, k, v, o, lse, S, Hq, Hkv, D, softmax_scale);
+  if (rc != H3ATTN_OK) return rc;
+  if ((flags & ~(H3ATTN_NONCAUSAL | H3ATTN_O_HEAD_MAJOR)) != 0) return H3ATTN_ERR_UNSUPPORTED;
+  if (S == 0) return H3ATTN_OK;
+  if (!device_ok()) return H3ATTN_ERR_DEVICE;
+  FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.cu_seqlens = nullptr;
+  p.seq_len = S;
+  p.total_tokens = S;
+  p.num_seqs = 1;
+  p.hq = Hq;
+  p.hkv = Hkv;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.o_head_major = (flags & H3ATTN_O_HEAD_MAJOR) ? 1 : 0;
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  return (flags & H3ATTN_NONCAUSAL) ? dispatch<false, false>(D, Hq / Hkv, p, st)
+                                    : dispatch<false, true>(D, Hq / Hkv, p, st);
+}
+
 size_t h3attn_gqa_causal_splitkv_workspace_bytes(int S, int Hq, int D, int num_splits) {
   return split_workspace_layout(S, Hq, D, num_splits, nullptr);
 }
@@ -257,7 +283,8 @@ const char* h3attn_status_string(int status) {
       return "invalid shape: negative size, Hq not a multiple of Hkv, inconsistent offsets, "
              "tokens*Hq*D >= 2^31, or num_splits outside 1..64";
     case H3ATTN_ERR_UNSUPPORTED:
-      return "unsupported configuration: head dim must be 64 or 128 and Hq/Hkv 1, 2, 4 or 8";
+      return "unsupported configuration: head dim must be 64 or 128, Hq/Hkv 1, 2, 4 or 8, "
+             "and flags a combination of H3ATTN_NONCAUSAL and H3ATTN_O_HEAD_MAJOR";
     case H3ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case H3ATTN_ERR_SCALE: return "softmax_scale must be finite and > 0";
     case H3ATTN_ERR_LAUNCH: return "HIP kernel launch failed";

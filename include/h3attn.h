@@ -53,7 +53,8 @@ typedef enum {
   H3ATTN_ERR_NULL = 1,        /* a required pointer is NULL (tensors of a nonempty call, offsets) */
   H3ATTN_ERR_SHAPE = 2,       /* negative size, Hq not a multiple of Hkv, offsets inconsistent,
                                  or tokens * Hq * D >= 2^31 */
-  H3ATTN_ERR_UNSUPPORTED = 3, /* head dim not 64 or 128, or group size Hq/Hkv not 1, 2, 4 or 8 */
+  H3ATTN_ERR_UNSUPPORTED = 3, /* head dim not 64 or 128, group size Hq/Hkv not 1, 2, 4 or 8,
+                                 or unknown flag bits */
   H3ATTN_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
   H3ATTN_ERR_SCALE = 5,       /* softmax_scale not finite or not > 0 */
   H3ATTN_ERR_LAUNCH = 6,      /* the HIP kernel launch failed (hipGetLastError) */
@@ -81,6 +82,27 @@ typedef enum {
  */
 H3ATTN_API int h3attn_gqa_causal_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                           int S, int Hq, int Hkv, int D, float softmax_scale, void* hip_stream);
+
+/* Flags of h3attn_gqa_fwd. */
+#define H3ATTN_NONCAUSAL 1    /* every query attends to all S keys (no causal mask) */
+#define H3ATTN_O_HEAD_MAJOR 2 /* o is [Hq, S, D] instead of [S, Hq, D] */
+
+/*
+ * GQA forward over one sequence with options.  With flags == 0 it is exactly
+ * h3attn_gqa_causal_fwd.  H3ATTN_NONCAUSAL drops the causal mask: the
+ * bidirectional attention of the video DiT that runs after the encoder (the
+ * h3.c project README's SDPA; the vpipe issue "0.1.29: MiniMax-H3 bf16 refused on
+ * a 64 GB Mac ...", whose logs show 19316- and 34121-row forwards) -- x_j over all
+ * j = 0 .. S-1, LSE over all S keys.
+ * H3ATTN_O_HEAD_MAJOR writes o head-major, [Hq, S, D] (the README's profiling
+ * notes leave the SDPA output in [head, row, dimension] order); lse is [Hq, S]
+ * either way.
+ * Arguments, checks and errors as h3attn_gqa_causal_fwd; unknown flag bits return
+ * H3ATTN_ERR_UNSUPPORTED.
+ */
+H3ATTN_API int h3attn_gqa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int S, int Hq, int Hkv, int D, float softmax_scale, int flags,
+                              void* hip_stream);
 
 /*
  * Packed variable-length causal GQA forward: num_seqs independent sequences

@@ -65,6 +65,7 @@ class Workload:
     seed: int
     kind: str = "normal"
     varlen: bool = False
+    causal: bool = True
     note: str = field(default="", compare=False)
 
     @property
@@ -85,12 +86,17 @@ class Workload:
             np.int64)
 
     def kept_pairs_per_head(self) -> int:
-        """(query, key) pairs with key <= query inside each sequence."""
+        """(query, key) pairs a query head attends to: key <= query inside each sequence,
+        or every pair of the sequence for the bidirectional form."""
+        if not self.causal:
+            return int(sum(s * s for s in self.seqlens))
         return int(sum(s * (s + 1) // 2 for s in self.seqlens))
 
-    def causal_flop(self) -> int:
+    def flop(self) -> int:
         """Algorithmic FLOP: 2*D for Q.K plus 2*D for P.V per kept pair and query head."""
         return 4 * self.head_dim * self.n_q_heads * self.kept_pairs_per_head()
+
+    causal_flop = flop
 
     def algorithmic_bytes(self) -> int:
         """Q, K, V read once and O (bf16), LSE (fp32) written once."""
@@ -119,6 +125,20 @@ WORKLOADS = {
     )
 }
 
+# Bidirectional (non-causal) attention at the row counts the vpipe issue's logs show for
+# the video DiT ("first forward at 19316 rows", "a 34121-row forward").  The pages print no
+# head counts for the DiT; 32 heads of dim 128, one KV head per query head (MHA), is this
+# build's choice of a DiT layer.
+DIT_WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("dit_s19316_h32_d128", (19316,), 32, 32, 128, seed=7, causal=False,
+                 note="bidirectional, the DiT forward's 19316 rows"),
+        Workload("dit_s34121_h32_d128", (34121,), 32, 32, 128, seed=8, causal=False,
+                 note="bidirectional, the DiT forward's 34121 rows"),
+    )
+}
+
 # Shapes for the split-KV path only (not the pages' workloads): with a single KV head the
 # single-dispatch kernel has one workgroup per query block, 128 at S=4096, too few for
 # 256 compute units; splitting each block's KV range multiplies the workgroups.
@@ -129,6 +149,8 @@ SPLITKV_WORKLOADS = {
                  note="one KV head: too few query blocks to fill the GPU without splits"),
     )
 }
+
+ALL_WORKLOADS = {**WORKLOADS, **DIT_WORKLOADS, **SPLITKV_WORKLOADS}
 
 PRIMARY = "failing_s10231"
 
