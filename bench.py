@@ -223,8 +223,12 @@ def main():
     avg_launch_ms = float(per_launch.mean())
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
 
+    metric = METRIC
+    if w.name != workloads.PRIMARY or args.path != "fused":
+        metric = (f"{'causal' if w.causal else 'bidirectional'} GQA fwd TFLOP/s (bf16), "
+                  f"{w.name}, {args.path} path; oracle-match")
     result = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

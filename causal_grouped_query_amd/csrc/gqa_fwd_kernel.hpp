@@ -131,6 +131,7 @@ __host__ __device__ __forceinline__ int split_first_tile(int n, int s, int ns) {
 // fp32 / bf16 range, and O and l accumulate without overflow.
 constexpr float WEIGHT_SUM_LIMIT = 65536.0f;
 constexpr float LN2 = 0.693147180559945309417f;
+constexpr int kXcds = 8;   // accelerator complex dies of an MI355X; workgroup i runs on die i % 8
 
 template <int D_, int G_, int NW_, int BN_>
 struct FwdConfig {
@@ -238,12 +239,24 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   const int half = lane >> 5;    // which 8-wide slice of a 16-wide contraction step
   const int col = lane & 31;     // MFMA column = this lane's query row within the wave
 
-  // ---- work decode: KV head fastest (consecutive workgroups go to consecutive XCDs, so
-  // with 8 KV heads each XCD serves one head and keeps its K/V in its own L2), then
-  // sequence, then query block from the heaviest (last) one down.
+  // ---- work decode.  Consecutive workgroups go to consecutive XCDs (8 of them), each
+  // with its own L2.  When the KV heads divide evenly over the XCDs, XCD x serves heads
+  // x, x+8, x+16, ... one after the other, so all its concurrent workgroups stream the
+  // same head's K/V (with 8 KV heads: one head per XCD for the whole launch); otherwise
+  // the KV head is simply the fastest index.  Then split, sequence, and query block from
+  // the heaviest (last) one down.
   int bid = blockIdx.x;
-  const int g = bid % p.hkv;
-  bid /= p.hkv;
+  int g;
+  if (p.hkv % kXcds == 0) {
+    const int per_head = (int)(gridDim.x / p.hkv);    // workgroups of one KV head
+    const int xcd = bid % kXcds;
+    const int j = bid / kXcds;                        // index among this XCD's workgroups
+    g = xcd + kXcds * (j / per_head);
+    bid = j % per_head;
+  } else {
+    g = bid % p.hkv;
+    bid /= p.hkv;
+  }
   int split = 0;
   if constexpr (SPLIT) {
     split = bid % p.num_splits;
