@@ -79,6 +79,9 @@ class Oracle:
                                                  ctypes.c_float, p_i64, i64, p_f64, p_f64,
                                                  ctypes.c_int]
         lib.oracle_gqa_bidirectional.restype = ctypes.c_int
+        lib.oracle_qk_norm_rope.argtypes = [p_u16, i64, i64, i64, p_u16, ctypes.c_double,
+                                            ctypes.c_int, ctypes.c_double, p_i64, p_f64]
+        lib.oracle_qk_norm_rope.restype = ctypes.c_int
         lib.oracle_threads.argtypes = [ctypes.c_int]
         lib.oracle_threads.restype = ctypes.c_int
         self._lib = lib
@@ -161,6 +164,36 @@ class Oracle:
             raise ValueError(f"oracle: invalid arguments (code {rc})")
         return o, lse
 
+    def qk_norm_rope(self, x, weight=None, eps: float = 1e-6, rope: bool = True,
+                     theta: float = 1e6, positions=None):
+        """Q/K prologue of one tensor x [S, H, D] (bf16 bits): optional RMS norm with the
+        [D] bf16 weight, optional rotate-half RoPE at positions (default: token index).
+        Returns float64 [S, H, D]."""
+        x = _as_bits(x, "x")
+        if x.ndim != 3:
+            raise ValueError("oracle: x must be [S, H, D]")
+        S, H, D = x.shape
+        out = np.empty((S, H, D), dtype=np.float64)
+        w = None if weight is None else _as_bits(weight, "weight").reshape(-1)
+        if w is not None and w.size != D:
+            raise ValueError("oracle: weight must hold D values")
+        pos = None
+        if positions is not None:
+            pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int64).reshape(-1))
+            if pos.size != S:
+                raise ValueError("oracle: positions must hold S values")
+
+        def ptr(a, t):
+            return None if a is None else a.ctypes.data_as(ctypes.POINTER(t))
+
+        rc = self._lib.oracle_qk_norm_rope(ptr(x, ctypes.c_uint16), S, H, D,
+                                           ptr(w, ctypes.c_uint16), float(eps), int(bool(rope)),
+                                           float(theta), ptr(pos, ctypes.c_int64),
+                                           ptr(out, ctypes.c_double))
+        if rc != 0:
+            raise ValueError(f"oracle: invalid arguments (code {rc})")
+        return out
+
     def gqa_causal_keyrange(self, q, k, v, scale: float, key_begin: int, key_end: int,
                             tokens=None, threads: int = 0):
         """One sequence, keys restricted to [key_begin, key_end) (and j <= i).
@@ -233,6 +266,13 @@ def gqa_causal_keyrange(q, k, v, scale: float, key_begin: int, key_end: int, tok
 def gqa_bidirectional(q, k, v, scale: float, tokens=None, threads: int = 0):
     """Non-causal GQA in fp64; see :meth:`Oracle.gqa_bidirectional`."""
     return default().gqa_bidirectional(q, k, v, scale, tokens=tokens, threads=threads)
+
+
+def qk_norm_rope(x, weight=None, eps: float = 1e-6, rope: bool = True, theta: float = 1e6,
+                 positions=None):
+    """Q/K RMS norm + RoPE prologue in fp64; see :meth:`Oracle.qk_norm_rope`."""
+    return default().qk_norm_rope(x, weight=weight, eps=eps, rope=rope, theta=theta,
+                                  positions=positions)
 
 
 def merge_partials(o_parts, lse_parts):

@@ -42,6 +42,17 @@
  * same softmax without the causal mask: oracle_gqa_bidirectional lets every
  * query of a sequence see all S keys (j = 0 .. S-1), nothing else changes.
  *
+ * The step before attention: the h3.c project README ("Checkpoint layout and
+ * media pipeline") runs a fused QK-normalization / RoPE kernel on the DiT's
+ * Q and K rows.  The pages give no formulas; oracle_qk_norm_rope takes the
+ * plainest reading, the Qwen-family convention:
+ *   RMS norm of one (token, head) row x[0..D):  y_d = x_d / sqrt(mean_d(x_d^2) + eps) * w_d
+ *   rotary embedding (rotate-half pairs (i, i + D/2), i < D/2), position p:
+ *     a_i = p * theta^(-2i/D)
+ *     z_i       = y_i * cos(a_i) - y_{i+D/2} * sin(a_i)
+ *     z_{i+D/2} = y_{i+D/2} * cos(a_i) + y_i * sin(a_i)
+ * either step optional, all in double.
+ *
  * Parallelism: (token, head) items are independent; OpenMP spreads them over
  * threads.  This changes no arithmetic: each item's sums run in the same order
  * whatever the thread count.
@@ -277,6 +288,45 @@ int oracle_gqa_bidirectional(const uint16_t* q, const uint16_t* k, const uint16_
     free(scores);
   }
   return status;
+}
+
+/*
+ * Q/K prologue: x [S, H, D] bf16 bits -> out [S, H, D] doubles.
+ * weight: D bf16 bits of the norm weight, or NULL for no norm.  rope: 0 or 1.
+ * positions: S int64 positions, or NULL for p = token index.  D must be even when
+ * rope is set.  Returns 0 or a negative code for invalid arguments.
+ */
+int oracle_qk_norm_rope(const uint16_t* x, int64_t S, int64_t H, int64_t D,
+                        const uint16_t* weight, double eps, int rope, double theta,
+                        const int64_t* positions, double* out) {
+  if (!x || !out) return -1;
+  if (S < 0 || H < 1 || D < 1 || (rope && (D % 2 != 0 || !(theta > 0.0)))) return -2;
+  if (weight && !(eps >= 0.0)) return -2;
+  const int64_t half = D / 2;
+#pragma omp parallel for schedule(static)
+  for (int64_t row = 0; row < S * H; ++row) {
+    const int64_t t = row / H;
+    const uint16_t* xr = x + row * D;
+    double* o = out + row * D;
+    for (int64_t d = 0; d < D; ++d) o[d] = bf16_bits_to_double(xr[d]);
+    if (weight) {
+      double ss = 0.0;
+      for (int64_t d = 0; d < D; ++d) ss += o[d] * o[d];
+      const double inv = 1.0 / sqrt(ss / (double)D + eps);
+      for (int64_t d = 0; d < D; ++d) o[d] = o[d] * inv * bf16_bits_to_double(weight[d]);
+    }
+    if (rope) {
+      const double p = positions ? (double)positions[t] : (double)t;
+      for (int64_t i = 0; i < half; ++i) {
+        const double a = p * pow(theta, -2.0 * (double)i / (double)D);
+        const double c = cos(a), sn = sin(a);
+        const double lo = o[i], hi = o[i + half];
+        o[i] = lo * c - hi * sn;
+        o[i + half] = hi * c + lo * sn;
+      }
+    }
+  }
+  return 0;
 }
 
 /* Threads an OpenMP region would use with the given request (<= 0: default). */

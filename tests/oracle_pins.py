@@ -20,7 +20,11 @@ Each ``pin_*`` function takes an :class:`oracle.Oracle` and raises
   over a partition of the keys against the full result,
 * for the bidirectional (non-causal) form: dense matrices, torch's float64
   SDPA without the causal flag, Q = 0 (mean of all values, LSE = ln S), and
-  invariance under a permutation of the key/value rows.
+  invariance under a permutation of the key/value rows,
+* for the Q/K prologue: torch's float64 rms_norm, the mean-square closed form
+  and scale invariance of the norm, RoPE on unit vectors (the rotate-half
+  convention and the frequency exponent) and RoPE's relative-position and
+  length-preserving properties.
 
 ``tests/test_oracle_pins.py`` runs them on the real oracle and
 ``tests/test_oracle_mutations.py`` checks that each planted mistake in a copy
@@ -401,6 +405,74 @@ def pin_bidirectional_key_permutation(orc):
     assert np.allclose(lse, lse2, rtol=1e-13, atol=1e-12)
 
 
+def pin_rmsnorm_torch(orc):
+    """Norm only: torch's float64 rms_norm over the head dim with the same weight and eps."""
+    import torch
+
+    S, H, D = 9, 5, 64
+    x = normal_inputs(500, S, H, 1, D, sigma=3.0)[0]
+    w = _bits(np.random.Generator(np.random.PCG64(501)).uniform(0.5, 1.5, D))
+    for eps in (1e-6, 0.5):
+        out = orc.qk_norm_rope(x, weight=w, eps=eps, rope=False)
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(_f64(x)), (D,),
+                                           weight=torch.from_numpy(_f64(w)), eps=eps).numpy()
+        assert np.allclose(out, ref, rtol=1e-13, atol=1e-14), eps
+
+
+def pin_rmsnorm_closed_forms(orc):
+    """Unit weight: mean(y^2) = m / (m + eps) with m = mean(x^2); eps = 0: scaling x by a
+    power of two (exact in bf16) leaves y unchanged."""
+    S, H, D = 4, 3, 128
+    x = normal_inputs(510, S, H, 1, D)[0]
+    ones = _bits(np.ones(D))
+    eps = 0.25
+    y = orc.qk_norm_rope(x, weight=ones, eps=eps, rope=False)
+    m = (_f64(x) ** 2).mean(axis=2)
+    assert np.allclose((y ** 2).mean(axis=2), m / (m + eps), rtol=1e-13)
+    y0 = orc.qk_norm_rope(x, weight=ones, eps=0.0, rope=False)
+    y1 = orc.qk_norm_rope(_bits(_f64(x) * 8.0), weight=ones, eps=0.0, rope=False)
+    assert np.allclose(y0, y1, rtol=1e-14, atol=0)
+
+
+def pin_rope_unit_vectors(orc):
+    """RoPE on unit vectors e_i (i < D/2) at position p: the pair (i, i+D/2) becomes
+    (cos a, sin a) with a = p * theta^(-2i/D), everything else stays 0; position 0 is the
+    identity."""
+    import math
+
+    S, H, D, theta = 6, 1, 16, 10000.0
+    half = D // 2
+    for i in (0, 1, 5, half - 1):
+        x = np.zeros((S, H, D), dtype=np.float32)
+        x[:, :, i] = 1.0
+        positions = np.array([0, 1, 2, 7, 100, 34120])
+        z = orc.qk_norm_rope(_bits(x), rope=True, theta=theta, positions=positions)
+        for t, p in enumerate(positions):
+            a = p * theta ** (-2.0 * i / D)
+            exp = np.zeros(D)
+            exp[i], exp[i + half] = math.cos(a), math.sin(a)
+            assert np.allclose(z[t, 0], exp, rtol=0, atol=1e-12), (i, p)
+
+
+def pin_rope_relative_position(orc):
+    """<rope(q, m), rope(k, n)> depends on m - n only, and rope keeps each pair's length."""
+    S, H, D = 8, 2, 64
+    q = normal_inputs(520, S, H, 1, D)[0]
+    k = normal_inputs(521, S, H, 1, D)[0]
+    base = np.arange(S)
+    zq = orc.qk_norm_rope(q, rope=True, theta=1e6, positions=base)
+    zk = orc.qk_norm_rope(k, rope=True, theta=1e6, positions=base[::-1].copy())
+    zq2 = orc.qk_norm_rope(q, rope=True, theta=1e6, positions=base + 977)
+    zk2 = orc.qk_norm_rope(k, rope=True, theta=1e6, positions=base[::-1] + 977)
+    d1 = (zq * zk).sum(axis=2)
+    d2 = (zq2 * zk2).sum(axis=2)
+    assert np.allclose(d1, d2, rtol=1e-10, atol=1e-10)
+    Q = _f64(q)
+    pair_in = Q[..., : D // 2] ** 2 + Q[..., D // 2:] ** 2
+    pair_out = zq[..., : D // 2] ** 2 + zq[..., D // 2:] ** 2
+    assert np.allclose(pair_in, pair_out, rtol=1e-13, atol=1e-13)
+
+
 ALL_PINS = [
     pin_brute_force_dense,
     pin_torch_sdpa_float64,
@@ -420,4 +492,8 @@ ALL_PINS = [
     pin_bidirectional_torch_sdpa,
     pin_bidirectional_zero_query,
     pin_bidirectional_key_permutation,
+    pin_rmsnorm_torch,
+    pin_rmsnorm_closed_forms,
+    pin_rope_unit_vectors,
+    pin_rope_relative_position,
 ]

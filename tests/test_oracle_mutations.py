@@ -36,6 +36,15 @@ MUTANTS = {
                                 "lse_out[h * ntok + ti] = 0.0;"),
     "bidirectional_masked": ("scale, 0, S - 1, scores,", "scale, 0, pos, scores,"),
     "bidirectional_misses_last_key": ("scale, 0, S - 1, scores,", "scale, 0, S - 2 + (S == 1), scores,"),
+    "rope_sin_sign": ("o[i + half] = hi * c + lo * sn;", "o[i + half] = hi * c - lo * sn;"),
+    "rope_frequency_exponent": ("pow(theta, -2.0 * (double)i / (double)D)",
+                                "pow(theta, -1.0 * (double)i / (double)D)"),
+    "rope_adjacent_pairs": ("const double lo = o[i], hi = o[i + half];",
+                            "const double lo = o[i], hi = o[i ^ 1];"),
+    "norm_sum_not_mean": ("sqrt(ss / (double)D + eps)", "sqrt(ss + eps)"),
+    "norm_eps_outside_root": ("sqrt(ss / (double)D + eps)", "(sqrt(ss / (double)D) + eps)"),
+    "norm_weight_ignored": ("o[d] = o[d] * inv * bf16_bits_to_double(weight[d]);",
+                            "o[d] = o[d] * inv;"),
 }
 
 
