@@ -31,10 +31,12 @@ LIBRARY = os.path.join(PKG_DIR, "libh3attn.so")
 MAX_SPLITS = 64
 
 NONCAUSAL, O_HEAD_MAJOR = 1, 2   # flags of h3attn_gqa_fwd
+PROLOGUE_ROPE = 1                # flag of h3attn_qk_norm_rope
 
 EXPORTED = ("h3attn_gqa_causal_fwd", "h3attn_gqa_fwd", "h3attn_gqa_causal_varlen_fwd",
             "h3attn_gqa_causal_splitkv_fwd", "h3attn_gqa_causal_splitkv_workspace_bytes",
-            "h3attn_status_string", "h3attn_version", "h3attn_lds_bytes")
+            "h3attn_qk_norm_rope", "h3attn_status_string", "h3attn_version",
+            "h3attn_lds_bytes")
 
 _lock = threading.Lock()
 _lib = None
@@ -72,6 +74,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         lib.h3attn_gqa_causal_varlen_fwd.restype = i32
         lib.h3attn_gqa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
         lib.h3attn_gqa_fwd.restype = i32
+        lib.h3attn_qk_norm_rope.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, f32, f32,
+                                            vp, i32, vp]
+        lib.h3attn_qk_norm_rope.restype = i32
         sz = ctypes.c_size_t
         lib.h3attn_gqa_causal_splitkv_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                                       f32, i32, vp, sz, vp]
@@ -205,6 +210,49 @@ def gqa_fwd(q, k, v, causal: bool = True, head_major_out: bool = False,
     return out, lse
 
 
+def qk_norm_rope(q, k, q_norm_weight=None, k_norm_weight=None, eps: float = 1e-6,
+                 rope: bool = True, rope_theta: float = 1e6, positions=None, q_out=None,
+                 k_out=None, stream=None):
+    """Q/K prologue (h3attn_qk_norm_rope): per-head RMS norm (when a weight is given) and
+    rotate-half RoPE.  q [S,Hq,D], k [S,Hkv,D] bf16 on the GPU; weights bf16 [D];
+    positions an int32 GPU tensor [S] (default: token index).  Returns (q_out, k_out);
+    pass q_out=q, k_out=k to work in place."""
+    import torch
+
+    for name, t in (("q", q), ("k", k)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 3 \
+                or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError(f"h3attn: {name} must be a contiguous bf16 [S, H, D] GPU tensor")
+    S, Hq, D = q.shape
+    if k.shape[0] != S or k.shape[2] != D:
+        raise ValueError("h3attn: q [S,Hq,D] and k [S,Hkv,D] must agree on S and D")
+    Hkv = k.shape[1]
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    for name, t, ref in (("q_out", q_out, q), ("k_out", k_out, k)):
+        if t.shape != ref.shape or t.dtype != torch.bfloat16 or not t.is_contiguous() \
+                or t.device != ref.device:
+            raise ValueError(f"h3attn: {name} must be a contiguous bf16 tensor shaped like its input")
+    for name, t in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        if t is not None and (t.dtype != torch.bfloat16 or t.numel() != D or t.device != q.device
+                              or not t.is_contiguous()):
+            raise ValueError(f"h3attn: {name} must be a contiguous bf16 GPU tensor of D values")
+    if positions is not None and (positions.dtype != torch.int32 or positions.numel() != S
+                                  or positions.device != q.device
+                                  or not positions.is_contiguous()):
+        raise ValueError("h3attn: positions must be a contiguous int32 GPU tensor of S values")
+
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+
+    rc = load_library().h3attn_qk_norm_rope(
+        q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), S, Hq, Hkv, D,
+        ptr(q_norm_weight), ptr(k_norm_weight), float(eps), float(rope_theta), ptr(positions),
+        PROLOGUE_ROPE if rope else 0, _stream_handle(stream, q.device))
+    _check(rc)
+    return q_out, k_out
+
+
 def gqa_causal_varlen_fwd(q, k, v, cu_seqlens, max_seqlen: int,
                           softmax_scale: float | None = None, out=None, lse=None,
                           return_lse: bool = True, stream=None):
@@ -278,4 +326,5 @@ def gqa_causal_splitkv_fwd(q, k, v, num_splits: int, softmax_scale: float | None
 
 __all__ = ["gqa_causal_fwd", "gqa_fwd", "gqa_causal_varlen_fwd", "gqa_causal_splitkv_fwd",
            "splitkv_workspace_bytes", "status_string", "version", "lds_bytes", "load_library",
-           "H3AttnError", "LIBRARY", "EXPORTED", "MAX_SPLITS", "NONCAUSAL", "O_HEAD_MAJOR"]
+           "H3AttnError", "LIBRARY", "EXPORTED", "MAX_SPLITS", "NONCAUSAL", "O_HEAD_MAJOR",
+           "qk_norm_rope", "PROLOGUE_ROPE"]

@@ -16,6 +16,7 @@
 
 #include "gqa_fwd_kernel.hpp"
 #include "gqa_merge_kernel.hpp"
+#include "qk_prologue_kernel.hpp"
 #include "h3attn.h"
 
 namespace {
@@ -238,6 +239,52 @@ int h3attn_gqa_fwd(const void* q, const void* k, const void* v, void* o, float* 
                                     : dispatch<false, true>(D, Hq / Hkv, p, st);
 }
 
+int h3attn_qk_norm_rope(const void* q, const void* k, void* q_out, void* k_out, int S, int Hq,
+                        int Hkv, int D, const void* q_norm_weight, const void* k_norm_weight,
+                        float eps, float rope_theta, const int32_t* positions, int flags,
+                        void* hip_stream) {
+  if (S > 0 && (!q || !k || !q_out || !k_out)) return H3ATTN_ERR_NULL;
+  if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return H3ATTN_ERR_SHAPE;
+  if ((long long)S * (long long)(Hq > Hkv ? Hq : Hkv) * (long long)D >= (1LL << 31))
+    return H3ATTN_ERR_SHAPE;
+  if ((D != 64 && D != 128) || (flags & ~H3ATTN_PROLOGUE_ROPE) != 0)
+    return H3ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out) ||
+      (reinterpret_cast<uintptr_t>(q_norm_weight) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(k_norm_weight) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(positions) & 3u) != 0)
+    return H3ATTN_ERR_ALIGN;
+  const bool rope = (flags & H3ATTN_PROLOGUE_ROPE) != 0;
+  if ((q_norm_weight || k_norm_weight) && (!std::isfinite(eps) || eps < 0.0f))
+    return H3ATTN_ERR_SCALE;
+  if (rope && (!std::isfinite(rope_theta) || !(rope_theta > 0.0f))) return H3ATTN_ERR_SCALE;
+  if (S == 0) return H3ATTN_OK;
+  if (!device_ok()) return H3ATTN_ERR_DEVICE;
+  h3attn::PrologueParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.q_out = static_cast<uint16_t*>(q_out);
+  p.k_out = static_cast<uint16_t*>(k_out);
+  p.q_weight = static_cast<const uint16_t*>(q_norm_weight);
+  p.k_weight = static_cast<const uint16_t*>(k_norm_weight);
+  p.positions = positions;
+  p.seq_len = S;
+  p.hq = Hq;
+  p.hkv = Hkv;
+  p.eps = eps;
+  p.theta = (double)rope_theta;
+  p.rope = rope ? 1 : 0;
+  const unsigned blocks = (unsigned)((S + h3attn::PROLOGUE_TOKENS - 1) / h3attn::PROLOGUE_TOKENS);
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (D == 128)
+    hipLaunchKernelGGL((h3attn::qk_prologue_kernel<128>), dim3(blocks),
+                       dim3(h3attn::PROLOGUE_THREADS), 0, st, p);
+  else
+    hipLaunchKernelGGL((h3attn::qk_prologue_kernel<64>), dim3(blocks),
+                       dim3(h3attn::PROLOGUE_THREADS), 0, st, p);
+  return hipGetLastError() == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
+}
+
 size_t h3attn_gqa_causal_splitkv_workspace_bytes(int S, int Hq, int D, int num_splits) {
   return split_workspace_layout(S, Hq, D, num_splits, nullptr);
 }
@@ -286,7 +333,9 @@ const char* h3attn_status_string(int status) {
       return "unsupported configuration: head dim must be 64 or 128, Hq/Hkv 1, 2, 4 or 8, "
              "and flags a combination of H3ATTN_NONCAUSAL and H3ATTN_O_HEAD_MAJOR";
     case H3ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
-    case H3ATTN_ERR_SCALE: return "softmax_scale must be finite and > 0";
+    case H3ATTN_ERR_SCALE:
+      return "softmax_scale must be finite and > 0 (prologue: eps finite and >= 0, rope_theta "
+             "finite and > 0)";
     case H3ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
     case H3ATTN_ERR_DEVICE: return "no usable gfx950 device is current";
     case H3ATTN_ERR_WORKSPACE:

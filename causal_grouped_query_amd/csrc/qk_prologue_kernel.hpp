@@ -1,0 +1,132 @@
+// qk_prologue_kernel.hpp -- gfx950 kernel for the step before attention: per-head RMS
+// norm of the Q and K rows and the rotary position embedding, in one pass over Q and K.
+//
+// The h3.c project README ("Checkpoint layout and media pipeline") runs a fused
+// QK-normalization / RoPE kernel on the DiT's Q and K rows; its profiling notes fold the
+// Q/K normalization and RoPE into the QKV projection.  The pages give no formulas; this
+// kernel computes the Qwen-family convention:
+//   y_d = x_d / sqrt(mean_d(x_d^2) + eps) * w_d                   (when a weight is given)
+//   a_i = p * theta^(-2i/D),  i < D/2, p the token's position
+//   z_i = y_i cos a_i - y_{i+D/2} sin a_i,  z_{i+D/2} = y_{i+D/2} cos a_i + y_i sin a_i
+// in fp32 with one bf16 rounding at the end; the angles and their cos / sin are computed
+// in fp64 (positions reach 10^4-10^5, where fp32 angles would lose ~10^-3 rad).
+//
+// HBM-bound streaming: one workgroup per TOKENS tokens.  Its threads first compute the
+// cos / sin of every (token, pair) of the block into LDS (one fp64 sincos each), then
+// each (token, head) row is handled by D/8 lanes; lane l holds the four elements
+// 4l..4l+3 and their rotation partners D/2+4l..D/2+4l+3 (two 8-byte loads), so the
+// rotation needs no data exchange and only the row's sum of squares is reduced across
+// the row's lanes (butterfly of D/8 lanes).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3attn {
+
+struct PrologueParams {
+  const uint16_t* q;        // [S, hq, D] bf16
+  const uint16_t* k;        // [S, hkv, D] bf16
+  uint16_t* q_out;          // [S, hq, D] bf16 (may be q)
+  uint16_t* k_out;          // [S, hkv, D] bf16 (may be k)
+  const uint16_t* q_weight; // [D] bf16 or nullptr (no norm of Q)
+  const uint16_t* k_weight; // [D] bf16 or nullptr (no norm of K)
+  const int32_t* positions; // [S] or nullptr (position = token index)
+  int seq_len, hq, hkv;
+  float eps;
+  double theta;
+  int rope;                 // 0: no rotary embedding
+};
+
+constexpr int PROLOGUE_THREADS = 256;
+constexpr int PROLOGUE_TOKENS = 4;
+
+template <int D>
+__global__ __launch_bounds__(PROLOGUE_THREADS) void qk_prologue_kernel(PrologueParams p) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+  typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+  constexpr int HALF = D / 2;
+  constexpr int LANES_ROW = D / 8;                   // lanes per (token, head) row
+  constexpr int ROWS_PASS = PROLOGUE_THREADS / LANES_ROW;
+  __shared__ float cs[PROLOGUE_TOKENS][HALF][2];     // cos, sin per (token, pair)
+
+  const int t0 = blockIdx.x * PROLOGUE_TOKENS;
+  const int ntok = min(PROLOGUE_TOKENS, p.seq_len - t0);
+
+  if (p.rope) {
+    for (int e = threadIdx.x; e < PROLOGUE_TOKENS * HALF; e += PROLOGUE_THREADS) {
+      const int tt = e / HALF, i = e % HALF;
+      if (tt < ntok) {
+        const int tok = t0 + tt;
+        const double pos = p.positions ? (double)p.positions[tok] : (double)tok;
+        const double a = pos * pow(p.theta, -2.0 * (double)i / (double)D);
+        double sn, c;
+        sincos(a, &sn, &c);
+        cs[tt][i][0] = (float)c;
+        cs[tt][i][1] = (float)sn;
+      }
+    }
+    __syncthreads();
+  }
+
+  const int li = threadIdx.x % LANES_ROW;            // lane within the row
+  const int rows_tok = p.hq + p.hkv;
+  const int rows = ntok * rows_tok;
+  // every lane of a row group runs the same number of iterations (rows is uniform), so
+  // the butterfly below always has all its lanes
+  for (int r0 = 0; r0 < rows; r0 += ROWS_PASS) {
+    const int r = r0 + threadIdx.x / LANES_ROW;
+    const bool live = r < rows;
+    const int tt = live ? r / rows_tok : 0;
+    const int h = live ? r % rows_tok : 0;
+    const bool is_q = h < p.hq;
+    const int tok = t0 + tt;
+    const uint16_t* src = is_q ? p.q + ((size_t)tok * p.hq + h) * D
+                               : p.k + ((size_t)tok * p.hkv + (h - p.hq)) * D;
+    uint16_t* dst = is_q ? p.q_out + ((size_t)tok * p.hq + h) * D
+                         : p.k_out + ((size_t)tok * p.hkv + (h - p.hq)) * D;
+    const uint16_t* w = is_q ? p.q_weight : p.k_weight;
+
+    f32x4v lo = {0.0f, 0.0f, 0.0f, 0.0f}, hi = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (live) {
+      lo = __builtin_convertvector(__builtin_bit_cast(bf16x4v, *(const u32x2v*)(src + 4 * li)),
+                                   f32x4v);
+      hi = __builtin_convertvector(
+          __builtin_bit_cast(bf16x4v, *(const u32x2v*)(src + HALF + 4 * li)), f32x4v);
+    }
+    if (w != nullptr) {   // uniform over a row (depends on is_q only)
+      float ss = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ss += lo[t] * lo[t] + hi[t] * hi[t];
+#pragma unroll
+      for (int m = 1; m < LANES_ROW; m <<= 1) ss += __shfl_xor(ss, m, LANES_ROW);
+      const float inv = 1.0f / __builtin_sqrtf(ss / (float)D + p.eps);
+      if (live) {
+        const f32x4v wl = __builtin_convertvector(
+            __builtin_bit_cast(bf16x4v, *(const u32x2v*)(w + 4 * li)), f32x4v);
+        const f32x4v wh = __builtin_convertvector(
+            __builtin_bit_cast(bf16x4v, *(const u32x2v*)(w + HALF + 4 * li)), f32x4v);
+        lo = lo * inv * wl;
+        hi = hi * inv * wh;
+      }
+    }
+    if (!live) continue;
+    if (p.rope) {
+      f32x4v zl, zh;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float c = cs[tt][4 * li + t][0], sn = cs[tt][4 * li + t][1];
+        zl[t] = lo[t] * c - hi[t] * sn;
+        zh[t] = hi[t] * c + lo[t] * sn;
+      }
+      lo = zl;
+      hi = zh;
+    }
+    *(u32x2v*)(dst + 4 * li) = __builtin_bit_cast(u32x2v, __builtin_convertvector(lo, bf16x4v));
+    *(u32x2v*)(dst + HALF + 4 * li) =
+        __builtin_bit_cast(u32x2v, __builtin_convertvector(hi, bf16x4v));
+  }
+}
+
+}  // namespace h3attn

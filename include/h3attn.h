@@ -164,6 +164,33 @@ H3ATTN_API int h3attn_gqa_causal_splitkv_fwd(const void* q, const void* k, const
 H3ATTN_API size_t h3attn_gqa_causal_splitkv_workspace_bytes(int S, int Hq, int D,
                                                             int num_splits);
 
+/* Flag of h3attn_qk_norm_rope. */
+#define H3ATTN_PROLOGUE_ROPE 1  /* apply the rotary position embedding */
+
+/*
+ * Q/K prologue: the step before attention that the h3.c project README runs as a
+ * fused QK-normalization / RoPE kernel ("Checkpoint layout and media pipeline").  The
+ * pages give no formulas; this computes the Qwen-family convention on every
+ * (token, head) row x[0..D) of q [S, Hq, D] and k [S, Hkv, D] (bf16):
+ *   RMS norm (when the tensor's weight pointer is non-NULL):
+ *       y_d = x_d / sqrt(mean_d(x_d^2) + eps) * w_d,   w: D bf16 values
+ *   rotary embedding (flags & H3ATTN_PROLOGUE_ROPE), rotate-half pairs (i, i+D/2):
+ *       a_i = p * rope_theta^(-2i/D),  p = positions[token] (int32 [S] on the device)
+ *             or the token index when positions == NULL
+ *       z_i = y_i cos a_i - y_{i+D/2} sin a_i,   z_{i+D/2} = y_{i+D/2} cos a_i + y_i sin a_i
+ * in fp32 (angles, cos and sin in fp64) with one bf16 rounding per output element.
+ * q_out / k_out have q's / k's shapes and may equal q / k (in place).  D in {64, 128}.
+ * Pointers: tensors 16-byte aligned, weights 8-byte aligned, positions 4-byte aligned,
+ * all DEVICE memory.  eps must be finite and >= 0 when a weight is given (a row of
+ * zeros with eps = 0 gives NaN, as the definition does); rope_theta finite and > 0 when
+ * RoPE is on (else H3ATTN_ERR_SCALE).  S == 0 is a no-op.  HBM-bound: it reads and
+ * writes every Q and K element once.
+ */
+H3ATTN_API int h3attn_qk_norm_rope(const void* q, const void* k, void* q_out, void* k_out, int S,
+                                   int Hq, int Hkv, int D, const void* q_norm_weight,
+                                   const void* k_norm_weight, float eps, float rope_theta,
+                                   const int32_t* positions, int flags, void* hip_stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 H3ATTN_API const char* h3attn_status_string(int status);
 
