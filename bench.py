@@ -42,9 +42,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=workloads.PRIMARY,
                     choices=sorted(workloads.ALL_WORKLOADS))
-    ap.add_argument("--path", default="fused", choices=("fused", "splitkv"),
+    ap.add_argument("--path", default="fused", choices=("fused", "splitkv", "prologue"),
                     help="fused: one kernel per call (the default, the benchmarked path); "
-                         "splitkv: per-split partials through a workspace, then a merge kernel")
+                         "splitkv: per-split partials through a workspace, then a merge kernel; "
+                         "prologue: the Q/K RMS norm + RoPE kernel alone (HBM-bound)")
     ap.add_argument("--splits", type=int, default=4, help="KV splits of the splitkv path")
     ap.add_argument("--head-major", action="store_true",
                     help="bidirectional workloads: write O as [Hq, S, D]")
@@ -150,6 +151,79 @@ def cpu_baseline(inp, w, target_s: float):
     }
 
 
+def bench_prologue(args, w, inp, torch, h3):
+    """The Q/K prologue (RMS norm with synthetic weights + RoPE, theta 1e6) on the workload's
+    Q and K: HBM-bound, reported in GB/s of algorithmic traffic against 8 TB/s."""
+    HBM_PEAK_GBS = 8000.0
+    D = w.head_dim
+    rng = np.random.Generator(np.random.PCG64(w.seed + 900))
+    wq_bits = workloads.f32_to_bf16_bits(rng.uniform(0.5, 1.5, D).astype(np.float32))
+    wk_bits = workloads.f32_to_bf16_bits(rng.uniform(0.5, 1.5, D).astype(np.float32))
+    q, k = to_device(inp["q"], torch), to_device(inp["k"], torch)
+    wq, wk = to_device(wq_bits, torch), to_device(wk_bits, torch)
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        h3.qk_norm_rope(q, k, wq, wk, eps=1e-6, rope=True, rope_theta=1e6, q_out=qo, k_out=ko,
+                        stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per_launch = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    ms_per_step = starts[0].elapsed_time(ends[-1]) / args.steps
+    T = w.total_tokens
+    elems = T * (w.n_q_heads + w.n_kv_heads) * D
+    nbytes = 2 * elems * 2 + 2 * 2 * D                     # read + write bf16, two weights
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (float(per_launch.mean()) * 1e-3) / 1e9
+    result = {
+        "metric": f"Q/K RMS norm + RoPE prologue GB/s (bf16), {w.name}",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "total_tokens": T, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": D, "path": "prologue",
+                   "norm": "RMS, synthetic U(0.5,1.5) weights, eps 1e-6", "rope_theta": 1e6},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "qk_prologue_kernel",
+                     "avg_launch_ms": round(float(per_launch.mean()), 5),
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_check or not args.no_cpu_baseline:
+        import oracle
+
+        t0 = time.perf_counter()
+        rq = oracle.qk_norm_rope(inp["q"], weight=wq_bits, eps=1e-6, rope=True, theta=1e6)
+        rk = oracle.qk_norm_rope(inp["k"], weight=wk_bits, eps=1e-6, rope=True, theta=1e6)
+        dt = time.perf_counter() - t0
+        worst = 0.0
+        for gpu, ref in ((qo, rq), (ko, rk)):
+            g = gpu.float().cpu().double().numpy()
+            rms = np.sqrt((ref ** 2).mean(axis=-1, keepdims=True))
+            bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -16 * rms
+            worst = max(worst, float((np.abs(g - ref) / bound).max()))
+        if not args.no_check:
+            result["oracle_match"] = {"elements": int(elems), "worst_err_over_bound": worst,
+                                      "bound": "2^-8 |exact| + 2^-16 row RMS",
+                                      "pass": bool(worst <= 1.0)}
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = {"value": nbytes / dt / 1e9, "unit": "GB/s",
+                                      "cores": oracle.threads(), "kind": "oracle",
+                                      "sample": f"the full Q and K of {w.name} ({elems} elements) "
+                                                f"in {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -172,6 +246,9 @@ def main():
     log(f"workload {w.name}: seqlens={w.seqlens} Hq={w.n_q_heads} Hkv={w.n_kv_heads} "
         f"D={w.head_dim}")
     inp = workloads.generate(w)
+    if args.path == "prologue":
+        bench_prologue(args, w, inp, torch, h3)
+        return
     q, k, v = to_device(inp["q"], torch), to_device(inp["k"], torch), to_device(inp["v"], torch)
     o = (torch.empty((w.n_q_heads, w.total_tokens, w.head_dim), dtype=torch.bfloat16,
                      device="cuda") if args.head_major else torch.empty_like(q))

@@ -250,8 +250,8 @@ int h3attn_qk_norm_rope(const void* q, const void* k, void* q_out, void* k_out, 
   if ((D != 64 && D != 128) || (flags & ~H3ATTN_PROLOGUE_ROPE) != 0)
     return H3ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out) ||
-      (reinterpret_cast<uintptr_t>(q_norm_weight) & 7u) != 0 ||
-      (reinterpret_cast<uintptr_t>(k_norm_weight) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(q_norm_weight) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(k_norm_weight) & 15u) != 0 ||
       (reinterpret_cast<uintptr_t>(positions) & 3u) != 0)
     return H3ATTN_ERR_ALIGN;
   const bool rope = (flags & H3ATTN_PROLOGUE_ROPE) != 0;

@@ -13,10 +13,10 @@
 //
 // HBM-bound streaming: one workgroup per TOKENS tokens.  Its threads first compute the
 // cos / sin of every (token, pair) of the block into LDS (one fp64 sincos each), then
-// each (token, head) row is handled by D/8 lanes; lane l holds the four elements
-// 4l..4l+3 and their rotation partners D/2+4l..D/2+4l+3 (two 8-byte loads), so the
+// each (token, head) row is handled by D/16 lanes; lane l holds the eight elements
+// 8l..8l+7 and their rotation partners D/2+8l..D/2+8l+7 (two 16-byte loads), so the
 // rotation needs no data exchange and only the row's sum of squares is reduced across
-// the row's lanes (butterfly of D/8 lanes).
+// the row's lanes (butterfly of D/16 lanes).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,15 +39,15 @@ struct PrologueParams {
 };
 
 constexpr int PROLOGUE_THREADS = 256;
-constexpr int PROLOGUE_TOKENS = 4;
+constexpr int PROLOGUE_TOKENS = 8;
 
 template <int D>
 __global__ __launch_bounds__(PROLOGUE_THREADS) void qk_prologue_kernel(PrologueParams p) {
-  typedef float f32x4v __attribute__((ext_vector_type(4)));
-  typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
-  typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+  typedef float f32x8v __attribute__((ext_vector_type(8)));
+  typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+  typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
   constexpr int HALF = D / 2;
-  constexpr int LANES_ROW = D / 8;                   // lanes per (token, head) row
+  constexpr int LANES_ROW = D / 16;                  // lanes per (token, head) row
   constexpr int ROWS_PASS = PROLOGUE_THREADS / LANES_ROW;
   __shared__ float cs[PROLOGUE_TOKENS][HALF][2];     // cos, sin per (token, pair)
 
@@ -73,59 +73,73 @@ __global__ __launch_bounds__(PROLOGUE_THREADS) void qk_prologue_kernel(PrologueP
   const int li = threadIdx.x % LANES_ROW;            // lane within the row
   const int rows_tok = p.hq + p.hkv;
   const int rows = ntok * rows_tok;
-  // every lane of a row group runs the same number of iterations (rows is uniform), so
-  // the butterfly below always has all its lanes
-  for (int r0 = 0; r0 < rows; r0 += ROWS_PASS) {
-    const int r = r0 + threadIdx.x / LANES_ROW;
-    const bool live = r < rows;
-    const int tt = live ? r / rows_tok : 0;
-    const int h = live ? r % rows_tok : 0;
-    const bool is_q = h < p.hq;
-    const int tok = t0 + tt;
-    const uint16_t* src = is_q ? p.q + ((size_t)tok * p.hq + h) * D
-                               : p.k + ((size_t)tok * p.hkv + (h - p.hq)) * D;
-    uint16_t* dst = is_q ? p.q_out + ((size_t)tok * p.hq + h) * D
-                         : p.k_out + ((size_t)tok * p.hkv + (h - p.hq)) * D;
-    const uint16_t* w = is_q ? p.q_weight : p.k_weight;
-
-    f32x4v lo = {0.0f, 0.0f, 0.0f, 0.0f}, hi = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (live) {
-      lo = __builtin_convertvector(__builtin_bit_cast(bf16x4v, *(const u32x2v*)(src + 4 * li)),
-                                   f32x4v);
-      hi = __builtin_convertvector(
-          __builtin_bit_cast(bf16x4v, *(const u32x2v*)(src + HALF + 4 * li)), f32x4v);
-    }
-    if (w != nullptr) {   // uniform over a row (depends on is_q only)
-      float ss = 0.0f;
+  // Each lane group handles RU rows per pass, all loads issued before any arithmetic
+  // (memory-level parallelism).  Every lane of a row group runs the same iterations (rows
+  // is uniform over the workgroup), so the butterflies below always have all their lanes.
+  constexpr int RU = 4;
+  for (int r0 = 0; r0 < rows; r0 += ROWS_PASS * RU) {
+    f32x8v lo[RU], hi[RU];
+    int rr[RU];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) ss += lo[t] * lo[t] + hi[t] * hi[t];
-#pragma unroll
-      for (int m = 1; m < LANES_ROW; m <<= 1) ss += __shfl_xor(ss, m, LANES_ROW);
-      const float inv = 1.0f / __builtin_sqrtf(ss / (float)D + p.eps);
-      if (live) {
-        const f32x4v wl = __builtin_convertvector(
-            __builtin_bit_cast(bf16x4v, *(const u32x2v*)(w + 4 * li)), f32x4v);
-        const f32x4v wh = __builtin_convertvector(
-            __builtin_bit_cast(bf16x4v, *(const u32x2v*)(w + HALF + 4 * li)), f32x4v);
-        lo = lo * inv * wl;
-        hi = hi * inv * wh;
+    for (int u = 0; u < RU; ++u) {
+      const int r = r0 + u * ROWS_PASS + threadIdx.x / LANES_ROW;
+      rr[u] = r;
+      lo[u] = f32x8v{};
+      hi[u] = f32x8v{};
+      if (r < rows) {
+        const int tt = r / rows_tok, h = r % rows_tok, tok = t0 + tt;
+        const uint16_t* src = h < p.hq ? p.q + ((size_t)tok * p.hq + h) * D
+                                       : p.k + ((size_t)tok * p.hkv + (h - p.hq)) * D;
+        lo[u] = __builtin_convertvector(
+            __builtin_bit_cast(bf16x8v, *(const u32x4v*)(src + 8 * li)), f32x8v);
+        hi[u] = __builtin_convertvector(
+            __builtin_bit_cast(bf16x8v, *(const u32x4v*)(src + HALF + 8 * li)), f32x8v);
       }
     }
-    if (!live) continue;
-    if (p.rope) {
-      f32x4v zl, zh;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float c = cs[tt][4 * li + t][0], sn = cs[tt][4 * li + t][1];
-        zl[t] = lo[t] * c - hi[t] * sn;
-        zh[t] = hi[t] * c + lo[t] * sn;
+    for (int u = 0; u < RU; ++u) {
+      const int r = rr[u];
+      const bool live = r < rows;
+      const int tt = live ? r / rows_tok : 0;
+      const int h = live ? r % rows_tok : 0;
+      const bool is_q = h < p.hq;
+      const int tok = t0 + tt;
+      const uint16_t* w = is_q ? p.q_weight : p.k_weight;
+      if (w != nullptr) {   // uniform over a row group (depends on is_q only)
+        float ss = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) ss += lo[u][t] * lo[u][t] + hi[u][t] * hi[u][t];
+#pragma unroll
+        for (int m = 1; m < LANES_ROW; m <<= 1) ss += __shfl_xor(ss, m, LANES_ROW);
+        const float inv = 1.0f / __builtin_sqrtf(ss / (float)D + p.eps);
+        if (live) {
+          const f32x8v wl = __builtin_convertvector(
+              __builtin_bit_cast(bf16x8v, *(const u32x4v*)(w + 8 * li)), f32x8v);
+          const f32x8v wh = __builtin_convertvector(
+              __builtin_bit_cast(bf16x8v, *(const u32x4v*)(w + HALF + 8 * li)), f32x8v);
+          lo[u] = lo[u] * inv * wl;
+          hi[u] = hi[u] * inv * wh;
+        }
       }
-      lo = zl;
-      hi = zh;
+      if (!live) continue;
+      if (p.rope) {
+        f32x8v zl, zh;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float c = cs[tt][8 * li + t][0], sn = cs[tt][8 * li + t][1];
+          zl[t] = lo[u][t] * c - hi[u][t] * sn;
+          zh[t] = hi[u][t] * c + lo[u][t] * sn;
+        }
+        lo[u] = zl;
+        hi[u] = zh;
+      }
+      uint16_t* dst = is_q ? p.q_out + ((size_t)tok * p.hq + h) * D
+                           : p.k_out + ((size_t)tok * p.hkv + (h - p.hq)) * D;
+      *(u32x4v*)(dst + 8 * li) =
+          __builtin_bit_cast(u32x4v, __builtin_convertvector(lo[u], bf16x8v));
+      *(u32x4v*)(dst + HALF + 8 * li) =
+          __builtin_bit_cast(u32x4v, __builtin_convertvector(hi[u], bf16x8v));
     }
-    *(u32x2v*)(dst + 4 * li) = __builtin_bit_cast(u32x2v, __builtin_convertvector(lo, bf16x4v));
-    *(u32x2v*)(dst + HALF + 4 * li) =
-        __builtin_bit_cast(u32x2v, __builtin_convertvector(hi, bf16x4v));
   }
 }
 

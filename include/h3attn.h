@@ -180,7 +180,7 @@ H3ATTN_API size_t h3attn_gqa_causal_splitkv_workspace_bytes(int S, int Hq, int D
  *       z_i = y_i cos a_i - y_{i+D/2} sin a_i,   z_{i+D/2} = y_{i+D/2} cos a_i + y_i sin a_i
  * in fp32 (angles, cos and sin in fp64) with one bf16 rounding per output element.
  * q_out / k_out have q's / k's shapes and may equal q / k (in place).  D in {64, 128}.
- * Pointers: tensors 16-byte aligned, weights 8-byte aligned, positions 4-byte aligned,
+ * Pointers: tensors and weights 16-byte aligned, positions 4-byte aligned,
  * all DEVICE memory.  eps must be finite and >= 0 when a weight is given (a row of
  * zeros with eps = 0 gives NaN, as the definition does); rope_theta finite and > 0 when
  * RoPE is on (else H3ATTN_ERR_SCALE).  S == 0 is a no-op.  HBM-bound: it reads and
