@@ -275,6 +275,45 @@ def qk_norm_rope(x, weight=None, eps: float = 1e-6, rope: bool = True, theta: fl
                                   positions=positions)
 
 
+def pool_tokens(x, begin: int, end: int, factor: int):
+    """Sequence-axis average pooling of the token span [begin, end) of x [T, C] (bf16 bits).
+
+    The issue "Qwen text encoder: sequence exceeds Metal threadgroup memory with reference
+    video + ref images (>=150 frames)", "Suggested fix directions" (second direction),
+    shortens the prompt by pooling the reference-video tokens before the encoder.  The
+    plainest reading, taken here: consecutive groups of ``factor`` tokens of the span
+    are replaced by their mean (the last group may be shorter and averages what it has);
+    tokens outside the span are kept.  Written out in float64 with plain loops over the
+    output rows.  Returns float64 [T - L + ceil(L / factor), C], L = end - begin.
+    """
+    x = _as_bits(x, "x")
+    if x.ndim != 2:
+        raise ValueError("oracle: x must be [T, C]")
+    T, C = x.shape
+    if not (0 <= begin <= end <= T) or factor < 1:
+        raise ValueError("oracle: need 0 <= begin <= end <= T and factor >= 1")
+    xf = (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    L = end - begin
+    groups = (L + factor - 1) // factor
+    out = np.empty((T - L + groups, C), dtype=np.float64)
+    row = 0
+    for t in range(begin):
+        out[row] = xf[t]
+        row += 1
+    for gi in range(groups):
+        a = begin + gi * factor
+        b = min(a + factor, end)
+        acc = np.zeros(C, dtype=np.float64)
+        for t in range(a, b):
+            acc += xf[t]
+        out[row] = acc / (b - a)
+        row += 1
+    for t in range(end, T):
+        out[row] = xf[t]
+        row += 1
+    return out
+
+
 def merge_partials(o_parts, lse_parts):
     """Combine attention results over disjoint key sets into the result over their union.
 

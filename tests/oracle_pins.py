@@ -24,7 +24,9 @@ Each ``pin_*`` function takes an :class:`oracle.Oracle` and raises
 * for the Q/K prologue: torch's float64 rms_norm, the mean-square closed form
   and scale invariance of the norm, RoPE on unit vectors (the rotate-half
   convention and the frequency exponent) and RoPE's relative-position and
-  length-preserving properties.
+  length-preserving properties,
+* for token pooling: identity at factor 1, equal tokens, numpy's reshape-mean
+  on divisible spans, a linear ramp's group midpoints, the output length.
 
 ``tests/test_oracle_pins.py`` runs them on the real oracle and
 ``tests/test_oracle_mutations.py`` checks that each planted mistake in a copy
@@ -473,6 +475,34 @@ def pin_rope_relative_position(orc):
     assert np.allclose(pair_in, pair_out, rtol=1e-13, atol=1e-13)
 
 
+def pin_pool_tokens(orc):
+    """Token pooling: factor 1 is the identity; a span of equal tokens pools to that token;
+    a divisible span equals numpy's reshape-mean; a linear ramp pools to the group
+    midpoints (closed form); the output length is T - L + ceil(L/f)."""
+    import oracle as _oracle
+
+    rng = np.random.Generator(np.random.PCG64(700))
+    T, C = 50, 24
+    x = _bits(rng.standard_normal((T, C)).astype(np.float32))
+    X = _f64(x)
+    assert np.array_equal(_oracle.pool_tokens(x, 5, 40, 1), X)
+    for begin, end, f in [(10, 34, 4), (0, 50, 5), (7, 7, 3), (3, 50, 7), (20, 29, 2)]:
+        out = _oracle.pool_tokens(x, begin, end, f)
+        L = end - begin
+        assert out.shape == (T - L + -(-L // f), C)
+        assert np.array_equal(out[:begin], X[:begin])
+        assert np.array_equal(out[out.shape[0] - (T - end):], X[end:])
+        if L % f == 0 and L > 0:
+            ref = X[begin:end].reshape(L // f, f, C).mean(axis=1)
+            assert np.allclose(out[begin:begin + L // f], ref, rtol=1e-15, atol=1e-15)
+    same = np.tile(x[:1], (T, 1))
+    assert np.array_equal(_oracle.pool_tokens(same, 4, 44, 6)[4:11], np.tile(X[:1], (7, 1)))
+    ramp = _bits(np.tile(np.arange(T, dtype=np.float32)[:, None], (1, C)))
+    out = _oracle.pool_tokens(ramp, 2, 47, 4)            # groups 2..5, 6..9, ..., 46
+    mids = [(a + min(a + 4, 47) - 1) / 2.0 for a in range(2, 47, 4)]
+    assert np.allclose(out[2:2 + len(mids), 0], mids, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [
     pin_brute_force_dense,
     pin_torch_sdpa_float64,
@@ -496,4 +526,5 @@ ALL_PINS = [
     pin_rmsnorm_closed_forms,
     pin_rope_unit_vectors,
     pin_rope_relative_position,
+    pin_pool_tokens,
 ]

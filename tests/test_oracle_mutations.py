@@ -109,3 +109,45 @@ def test_wrong_merge_is_caught(wrong, monkeypatch):
     monkeypatch.setattr(oracle, "merge_partials", wrong)
     with pytest.raises(AssertionError):
         pin_merge_of_key_partition(oracle.default())
+
+
+_RIGHT_POOL = oracle.pool_tokens
+
+
+def _pool_divides_by_factor(x, begin, end, factor):
+    """Mistake: the short last group is divided by the full factor."""
+    import numpy as np
+
+    out = _RIGHT_POOL(x, begin, end, factor)
+    L = end - begin
+    rem = L % factor
+    if rem:
+        out[begin + L // factor] *= rem / factor
+    return out
+
+
+def _pool_drops_tail(x, begin, end, factor):
+    """Mistake: the tokens after the span are not copied (output too short)."""
+    out = _RIGHT_POOL(x, begin, end, factor)
+    return out[: out.shape[0] - (x.shape[0] - end)] if end < x.shape[0] else out
+
+
+def _pool_first_of_group(x, begin, end, factor):
+    """Mistake: subsampling (first token of each group) instead of averaging."""
+    import numpy as np
+
+    xf = _RIGHT_POOL(x, 0, 0, 1)
+    out = _RIGHT_POOL(x, begin, end, factor)
+    g = (end - begin + factor - 1) // factor
+    out[begin:begin + g] = xf[begin:end:factor]
+    return out
+
+
+@pytest.mark.parametrize("wrong", [_pool_divides_by_factor, _pool_drops_tail,
+                                   _pool_first_of_group], ids=lambda f: f.__name__.lstrip("_"))
+def test_wrong_pooling_is_caught(wrong, monkeypatch):
+    from oracle_pins import pin_pool_tokens
+
+    monkeypatch.setattr(oracle, "pool_tokens", wrong)
+    with pytest.raises(AssertionError):
+        pin_pool_tokens(oracle.default())
