@@ -42,10 +42,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=workloads.PRIMARY,
                     choices=sorted(workloads.ALL_WORKLOADS))
-    ap.add_argument("--path", default="fused", choices=("fused", "splitkv", "prologue"),
+    ap.add_argument("--path", default="fused", choices=("fused", "splitkv", "prologue", "pool"),
                     help="fused: one kernel per call (the default, the benchmarked path); "
                          "splitkv: per-split partials through a workspace, then a merge kernel; "
-                         "prologue: the Q/K RMS norm + RoPE kernel alone (HBM-bound)")
+                         "prologue: the Q/K RMS norm + RoPE kernel alone (HBM-bound); "
+                         "pool: reference-video token pooling of the workload's prompt length")
     ap.add_argument("--splits", type=int, default=4, help="KV splits of the splitkv path")
     ap.add_argument("--head-major", action="store_true",
                     help="bidirectional workloads: write O as [Hq, S, D]")
@@ -224,6 +225,70 @@ def bench_prologue(args, w, inp, torch, h3):
     print(json.dumps(result), flush=True)
 
 
+def bench_pool(args, w, torch, h3):
+    """Token pooling of a prompt of the workload's length: the issue's ~7500 reference-video
+    tokens ([2300, 9800) of 10231) pooled by 4, C = 4096 synthetic embedding channels.
+    HBM-bound, reported in GB/s of algorithmic traffic against 8 TB/s."""
+    HBM_PEAK_GBS = 8000.0
+    T, C = w.total_tokens, 4096
+    begin, end, factor = min(2300, T), min(9800, T), 4
+    rng = np.random.Generator(np.random.PCG64(w.seed + 950))
+    x_bits = workloads.f32_to_bf16_bits(rng.standard_normal((T, C)).astype(np.float32))
+    x = to_device(x_bits, torch)
+    n = h3.pool_tokens_out_len(T, begin, end, factor)
+    out = torch.empty((n, C), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        h3.pool_tokens(x, begin, end, factor, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per_launch = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    ms_per_step = starts[0].elapsed_time(ends[-1]) / args.steps
+    nbytes = (T + n) * C * 2
+    achieved = nbytes / (float(per_launch.mean()) * 1e-3) / 1e9
+    result = {
+        "metric": f"reference-video token pooling GB/s (bf16), {T} tokens",
+        "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "total_tokens": T, "channels": C, "span": [begin, end],
+                   "factor": factor, "out_tokens": n, "path": "pool"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pool_tokens_kernel",
+                     "avg_launch_ms": round(float(per_launch.mean()), 5),
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_check or not args.no_cpu_baseline:
+        import oracle
+
+        t0 = time.perf_counter()
+        ref = oracle.pool_tokens(x_bits, begin, end, factor)
+        dt = time.perf_counter() - t0
+        g = out.float().cpu().double().numpy()
+        bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -20 * np.abs(ref).max()
+        worst = float((np.abs(g - ref) / bound).max())
+        if not args.no_check:
+            result["oracle_match"] = {"elements": int(n * C), "worst_err_over_bound": worst,
+                                      "pass": bool(worst <= 1.0)}
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1,
+                                      "kind": "oracle", "sample": f"the full [{T}, {C}] prompt, "
+                                      f"numpy float64 loops, in {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -245,6 +310,9 @@ def main():
         sys.exit(2)
     log(f"workload {w.name}: seqlens={w.seqlens} Hq={w.n_q_heads} Hkv={w.n_kv_heads} "
         f"D={w.head_dim}")
+    if args.path == "pool":
+        bench_pool(args, w, torch, h3)
+        return
     inp = workloads.generate(w)
     if args.path == "prologue":
         bench_prologue(args, w, inp, torch, h3)

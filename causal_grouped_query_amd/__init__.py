@@ -35,7 +35,8 @@ PROLOGUE_ROPE = 1                # flag of h3attn_qk_norm_rope
 
 EXPORTED = ("h3attn_gqa_causal_fwd", "h3attn_gqa_fwd", "h3attn_gqa_causal_varlen_fwd",
             "h3attn_gqa_causal_splitkv_fwd", "h3attn_gqa_causal_splitkv_workspace_bytes",
-            "h3attn_qk_norm_rope", "h3attn_status_string", "h3attn_version",
+            "h3attn_qk_norm_rope", "h3attn_pool_tokens", "h3attn_pool_tokens_out_len",
+            "h3attn_status_string", "h3attn_version",
             "h3attn_lds_bytes")
 
 _lock = threading.Lock()
@@ -77,6 +78,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         lib.h3attn_qk_norm_rope.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, f32, f32,
                                             vp, i32, vp]
         lib.h3attn_qk_norm_rope.restype = i32
+        lib.h3attn_pool_tokens.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp]
+        lib.h3attn_pool_tokens.restype = i32
+        lib.h3attn_pool_tokens_out_len.argtypes = [i32, i32, i32, i32]
+        lib.h3attn_pool_tokens_out_len.restype = i32
         sz = ctypes.c_size_t
         lib.h3attn_gqa_causal_splitkv_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                                       f32, i32, vp, sz, vp]
@@ -253,6 +258,34 @@ def qk_norm_rope(q, k, q_norm_weight=None, k_norm_weight=None, eps: float = 1e-6
     return q_out, k_out
 
 
+def pool_tokens_out_len(T: int, begin: int, end: int, factor: int) -> int:
+    """Length of :func:`pool_tokens`'s output (-1 for invalid arguments)."""
+    return int(load_library().h3attn_pool_tokens_out_len(int(T), int(begin), int(end),
+                                                         int(factor)))
+
+
+def pool_tokens(x, begin: int, end: int, factor: int, out=None, stream=None):
+    """Average-pool groups of ``factor`` tokens inside [begin, end) of x [T, C] (bf16 on the
+    GPU); tokens outside the span are copied.  Returns out [T_out, C]."""
+    import torch
+
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16 or x.dim() != 2 \
+            or not x.is_contiguous() or x.device.type != "cuda":
+        raise ValueError("h3attn: x must be a contiguous bf16 [T, C] GPU tensor")
+    T, C = x.shape
+    n = pool_tokens_out_len(T, begin, end, factor)
+    if n < 0:
+        raise H3AttnError(ERR_SHAPE, status_string(ERR_SHAPE))
+    if out is None:
+        out = torch.empty((n, C), dtype=torch.bfloat16, device=x.device)
+    elif out.shape != (n, C) or out.dtype != torch.bfloat16 or not out.is_contiguous() \
+            or out.device != x.device:
+        raise ValueError("h3attn: out must be a contiguous bf16 tensor [T_out, C]")
+    _check(load_library().h3attn_pool_tokens(x.data_ptr(), out.data_ptr(), T, C, int(begin),
+                                             int(end), int(factor), _stream_handle(stream, x.device)))
+    return out
+
+
 def gqa_causal_varlen_fwd(q, k, v, cu_seqlens, max_seqlen: int,
                           softmax_scale: float | None = None, out=None, lse=None,
                           return_lse: bool = True, stream=None):
@@ -327,4 +360,4 @@ def gqa_causal_splitkv_fwd(q, k, v, num_splits: int, softmax_scale: float | None
 __all__ = ["gqa_causal_fwd", "gqa_fwd", "gqa_causal_varlen_fwd", "gqa_causal_splitkv_fwd",
            "splitkv_workspace_bytes", "status_string", "version", "lds_bytes", "load_library",
            "H3AttnError", "LIBRARY", "EXPORTED", "MAX_SPLITS", "NONCAUSAL", "O_HEAD_MAJOR",
-           "qk_norm_rope", "PROLOGUE_ROPE"]
+           "qk_norm_rope", "PROLOGUE_ROPE", "pool_tokens", "pool_tokens_out_len"]

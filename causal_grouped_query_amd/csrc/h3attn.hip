@@ -16,6 +16,7 @@
 
 #include "gqa_fwd_kernel.hpp"
 #include "gqa_merge_kernel.hpp"
+#include "pool_tokens_kernel.hpp"
 #include "qk_prologue_kernel.hpp"
 #include "h3attn.h"
 
@@ -285,6 +286,35 @@ int h3attn_qk_norm_rope(const void* q, const void* k, void* q_out, void* k_out, 
   return hipGetLastError() == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
 }
 
+int h3attn_pool_tokens_out_len(int T, int begin, int end, int factor) {
+  if (T < 0 || begin < 0 || end < begin || end > T || factor < 1) return -1;
+  const int L = end - begin;
+  return T - L + (L + factor - 1) / factor;
+}
+
+int h3attn_pool_tokens(const void* x, void* out, int T, int C, int begin, int end, int factor,
+                       void* hip_stream) {
+  const int T_out = h3attn_pool_tokens_out_len(T, begin, end, factor);
+  if (T_out < 0 || C <= 0) return H3ATTN_ERR_SHAPE;
+  if ((long long)T * (long long)C >= (1LL << 31)) return H3ATTN_ERR_SHAPE;
+  if (C % 8 != 0) return H3ATTN_ERR_UNSUPPORTED;
+  if (T_out == 0) return H3ATTN_OK;
+  if (!x || !out) return H3ATTN_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out)) return H3ATTN_ERR_ALIGN;
+  if (!device_ok()) return H3ATTN_ERR_DEVICE;
+  h3attn::PoolParams p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.out = static_cast<uint16_t*>(out);
+  p.T = T;
+  p.C = C;
+  p.begin = begin;
+  p.end = end;
+  p.factor = factor;
+  hipLaunchKernelGGL(h3attn::pool_tokens_kernel, dim3((unsigned)T_out),
+                     dim3(h3attn::POOL_THREADS), 0, static_cast<hipStream_t>(hip_stream), p);
+  return hipGetLastError() == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
+}
+
 size_t h3attn_gqa_causal_splitkv_workspace_bytes(int S, int Hq, int D, int num_splits) {
   return split_workspace_layout(S, Hq, D, num_splits, nullptr);
 }
@@ -331,7 +361,7 @@ const char* h3attn_status_string(int status) {
              "tokens*Hq*D >= 2^31, or num_splits outside 1..64";
     case H3ATTN_ERR_UNSUPPORTED:
       return "unsupported configuration: head dim must be 64 or 128, Hq/Hkv 1, 2, 4 or 8, "
-             "and flags a combination of H3ATTN_NONCAUSAL and H3ATTN_O_HEAD_MAJOR";
+             "flags known to the entry point, and (token pooling) C a multiple of 8";
     case H3ATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case H3ATTN_ERR_SCALE:
       return "softmax_scale must be finite and > 0 (prologue: eps finite and >= 0, rope_theta "

@@ -191,6 +191,23 @@ H3ATTN_API int h3attn_qk_norm_rope(const void* q, const void* k, void* q_out, vo
                                    const void* k_norm_weight, float eps, float rope_theta,
                                    const int32_t* positions, int flags, void* hip_stream);
 
+/*
+ * Reference-video token pooling, the second fix direction of the issue ("Suggested fix
+ * directions": pool or down-sample the video tokens before the text encoder so the
+ * sequence gets shorter).  x [T, C] bf16 (token embeddings) -> out [T_out, C] bf16:
+ * inside the span [begin, end) every `factor` consecutive tokens are replaced by their
+ * mean (fp32 sum, one bf16 rounding; a shorter last group averages what it has); the
+ * tokens before and after the span are copied.  T_out = T - L + ceil(L / factor),
+ * L = end - begin (h3attn_pool_tokens_out_len).  0 <= begin <= end <= T, factor >= 1
+ * (else H3ATTN_ERR_SHAPE); C a multiple of 8 (else H3ATTN_ERR_UNSUPPORTED); x, out
+ * DEVICE memory, 16-byte aligned, not overlapping.  T_out == 0 is a no-op.
+ */
+H3ATTN_API int h3attn_pool_tokens(const void* x, void* out, int T, int C, int begin, int end,
+                                  int factor, void* hip_stream);
+
+/* Output length of h3attn_pool_tokens, or -1 for invalid arguments. */
+H3ATTN_API int h3attn_pool_tokens_out_len(int T, int begin, int end, int factor);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 H3ATTN_API const char* h3attn_status_string(int status);
 

@@ -1,0 +1,89 @@
+"""Reference-video token pooling against the oracle, through the C ABI entry
+h3attn_pool_tokens (needs a gfx950 GPU).
+
+Bound per element: the mean is summed in fp32 and rounded to bf16 once, so
+|gpu - exact| <= 2^-8 |exact| + 2^-20 * max |x| over the group's inputs; copied tokens are
+bit-exact.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import bits_of, to_device
+from workloads import bf16_bits_to_f32, f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import causal_grouped_query_amd as h3
+
+    h3.load_library()
+    return h3
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-test] {request.node.nodeid}", flush=True)
+    yield
+
+
+def _x(seed, T, C, sigma=1.0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return f32_to_bf16_bits((sigma * rng.standard_normal((T, C))).astype(np.float32))
+
+
+def _check(lib, x, begin, end, factor, what):
+    import torch
+
+    out = lib.pool_tokens(to_device(x), begin, end, factor)
+    torch.cuda.synchronize()
+    ref = oracle.pool_tokens(x, begin, end, factor)
+    g = bf16_bits_to_f32(bits_of(out)).astype(np.float64)
+    assert g.shape == ref.shape, what
+    X = bf16_bits_to_f32(x).astype(np.float64)
+    bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -20 * np.abs(X).max()
+    err = np.abs(g - ref)
+    print(f"[pool] {what}: out {g.shape}, max err {err.max():.3e}", flush=True)
+    assert np.all(err <= bound), what
+    # tokens outside the span are bit-exact copies
+    nb = begin
+    na = x.shape[0] - end
+    assert np.array_equal(bits_of(out)[:nb], x[:nb])
+    if na:
+        assert np.array_equal(bits_of(out)[-na:], x[end:])
+
+
+@pytest.mark.parametrize("T,C,begin,end,factor,seed", [
+    (16, 64, 2, 14, 4, 801),
+    (100, 128, 0, 100, 3, 802),
+    (37, 72, 5, 36, 7, 803),       # ragged last group, C not a multiple of 256*8
+    (50, 4096, 10, 10, 4, 804),    # empty span: a copy
+    (300, 2056, 17, 281, 2, 805),
+])
+def test_pool_small(lib, T, C, begin, end, factor, seed):
+    _check(lib, _x(seed, T, C), begin, end, factor, f"T={T} C={C} [{begin},{end}) f={factor}")
+
+
+def test_pool_factor_one_is_a_copy(lib):
+    import torch
+
+    x = _x(810, 64, 256)
+    out = lib.pool_tokens(to_device(x), 0, 64, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(out), x)
+
+
+def test_pool_issue_sized_prompt(lib):
+    """The issue's failing prompt: 10231 tokens of which ~7500 are reference-video tokens;
+    pooling the video span by 4 leaves 4606 tokens, under the old ~7700-token ceiling."""
+    T, C, begin, end, factor = 10231, 1024, 2300, 9800, 4
+    assert lib.pool_tokens_out_len(T, begin, end, factor) == 4606
+    _check(lib, _x(820, T, C, sigma=3.0), begin, end, factor, "issue-sized prompt")
