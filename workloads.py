@@ -189,6 +189,18 @@ def stress_inputs(seed: int, T: int, n_q_heads: int, n_kv_heads: int, head_dim: 
     return q, k, v, positions
 
 
+def device_normal_bf16(seed: int, shapes, device="cuda"):
+    """bf16 tensors of N(0,1) values drawn on the GPU with torch's seeded generator, one per
+    shape in ``shapes`` (in that order).  For sizes where host generation would dominate a
+    test (gigabytes); the oracle receives the same values by copying the bits back."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return tuple(torch.randn(tuple(sh), generator=g, device=device, dtype=torch.float32)
+                 .to(torch.bfloat16) for sh in shapes)
+
+
 def generate(w: Workload) -> dict:
     """All inputs of a workload: q, k, v (uint16 bits), cu_seqlens, scale."""
     T = w.total_tokens
