@@ -208,11 +208,17 @@ __device__ __forceinline__ void fill_tile_lds(const uint16_t* ksrc, const uint16
     // would otherwise wait for them before unrelated LDS reads of other stages.  The
     // kernel orders them itself (wait_vmem, then a workgroup barrier, before any read).
     // The s_nop covers the one wait state between an SALU write of M0 and its use as the
-    // LDS address of a buffer load.
+    // LDS address of a buffer load.  M0 is a register the compiler reserves; clang warns
+    // that a clobbered reserved register may not be preserved.  Nothing else in these
+    // kernels keeps a value in M0: tests/test_abi.py checks the built code object for any
+    // other M0 access, so the warning is silenced here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :: "v"(fill_off[n]), "s"(kr), "s"(kl) : "memory", "m0");
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :: "v"(fill_off[n]), "s"(vr), "s"(vl) : "memory", "m0");
+#pragma clang diagnostic pop
   }
 }
 
