@@ -249,8 +249,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
   // with its own L2.  When the KV heads divide evenly over the XCDs, XCD x serves heads
   // x, x+8, x+16, ... one after the other, so all its concurrent workgroups stream the
   // same head's K/V (with 8 KV heads: one head per XCD for the whole launch); otherwise
-  // the KV head is simply the fastest index.  Then split, sequence, and query block from
-  // the heaviest (last) one down.
+  // the KV head is simply the fastest index.  Then split, then query block from the
+  // heaviest (last) one down, then sequence: the sequences of a packed batch run one
+  // after another, so the workgroups an XCD runs at once stream one sequence's K/V
+  // through its L2 (interleaving the sequences multiplies that working set).
   int bid = blockIdx.x;
   int g;
   if (p.hkv % kXcds == 0) {
@@ -268,9 +270,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_causal_fwd_kernel(FwdParams
     split = bid % p.num_splits;
     bid /= p.num_splits;
   }
-  const int seq = bid % p.num_seqs;
-  bid /= p.num_seqs;
-  const int qblk = p.n_qblk - 1 - bid;
+  const int seq = bid / p.n_qblk;
+  const int qblk = p.n_qblk - 1 - bid % p.n_qblk;
 
   int start = 0, len = p.seq_len;
   if (VARLEN) {
