@@ -81,9 +81,11 @@ def test_pool_factor_one_is_a_copy(lib):
     assert np.array_equal(bits_of(out), x)
 
 
-def test_pool_issue_sized_prompt(lib):
+@pytest.mark.parametrize("C", [1024, 4096])
+def test_pool_issue_sized_prompt(lib, C):
     """The issue's failing prompt: 10231 tokens of which ~7500 are reference-video tokens;
-    pooling the video span by 4 leaves 4606 tokens, under the old ~7700-token ceiling."""
-    T, C, begin, end, factor = 10231, 1024, 2300, 9800, 4
+    pooling the video span by 4 leaves 4606 tokens, under the old ~7700-token ceiling.
+    C = 4096 is the configuration the benchmark times; every output element is checked."""
+    T, begin, end, factor = 10231, 2300, 9800, 4
     assert lib.pool_tokens_out_len(T, begin, end, factor) == 4606
-    _check(lib, _x(820, T, C, sigma=3.0), begin, end, factor, "issue-sized prompt")
+    _check(lib, _x(820, T, C, sigma=3.0), begin, end, factor, f"issue-sized prompt C={C}")
