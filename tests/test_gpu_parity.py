@@ -59,6 +59,11 @@ SMALL = [
     (517, 8, 4, 64, 110),
     (700, 8, 8, 128, 111),
     (1000, 16, 16, 128, 112),
+    (97, 16, 2, 64, 113),      # G = 8 at D = 64
+    (300, 32, 4, 64, 114),     # G = 8 at D = 64, several query blocks
+    (130, 32, 8, 64, 115),     # G = 4 at D = 64
+    (96, 64, 8, 128, 116),     # the 64/8/128 heads, exactly three 32-token query blocks
+    (1025, 64, 8, 128, 117),   # the 64/8/128 heads, one token past a 1024 boundary
 ]
 
 
