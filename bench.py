@@ -42,11 +42,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=workloads.PRIMARY,
                     choices=sorted(workloads.ALL_WORKLOADS))
-    ap.add_argument("--path", default="fused", choices=("fused", "splitkv", "prologue", "pool"),
+    ap.add_argument("--path", default="fused",
+                    choices=("fused", "splitkv", "prologue", "pool", "qpro"),
                     help="fused: one kernel per call (the default, the benchmarked path); "
                          "splitkv: per-split partials through a workspace, then a merge kernel; "
                          "prologue: the Q/K RMS norm + RoPE kernel alone (HBM-bound); "
-                         "pool: reference-video token pooling of the workload's prompt length")
+                         "pool: reference-video token pooling of the workload's prompt length; "
+                         "qpro: the Q/K prologue + causal forward, two passes vs Q fused")
     ap.add_argument("--splits", type=int, default=4, help="KV splits of the splitkv path")
     ap.add_argument("--head-major", action="store_true",
                     help="bidirectional workloads: write O as [Hq, S, D]")
@@ -73,18 +75,23 @@ def copy_probe(mib: int) -> None:
     print(json.dumps({"copy_probe_bytes": n}), flush=True)
 
 
+# the attention kernel's source (its statements and its launch configuration)
+KERNEL_SOURCES = ("gqa_fwd_kernel.hpp", "gqa_fwd_body.inc")
+
+
 def recorded_traffic():
     """HBM bytes per launch recorded for the current kernel source, or None.
 
     profiles/gqa_causal_fwd_s10231_hbm_traffic.txt holds a line
     `traffic_bytes_per_launch: N source_sha256: H`; the figure applies only while the
-    attention kernel's source (csrc/gqa_fwd_kernel.hpp, which also fixes its launch
-    configuration) still hashes to H."""
+    attention kernel's source (csrc/gqa_fwd_kernel.hpp and csrc/gqa_fwd_body.inc, which also
+    fix its launch configuration), hashed in that order, is still H."""
     import hashlib
 
-    with open(os.path.join(ROOT, "causal_grouped_query_amd", "csrc", "gqa_fwd_kernel.hpp"),
-              "rb") as f:
-        h = hashlib.sha256(f.read())
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "causal_grouped_query_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
     path = os.path.join(ROOT, "profiles", "gqa_causal_fwd_s10231_hbm_traffic.txt")
     try:
         with open(path) as f:
@@ -225,6 +232,85 @@ def bench_prologue(args, w, inp, torch, h3):
     print(json.dumps(result), flush=True)
 
 
+def bench_qpro(args, w, inp, torch, h3):
+    """The encoder's attention step with the Q/K prologue (RMS norm with synthetic weights +
+    RoPE, theta 1e6), two ways on the same inputs: the prologue kernel over Q and K then the
+    causal forward (two passes), and the K-only prologue then the causal forward that
+    normalises and rotates Q as it loads it (fused).  value = causal flop / fused step time."""
+    D = w.head_dim
+    rng = np.random.Generator(np.random.PCG64(w.seed + 900))
+    wq_bits = workloads.f32_to_bf16_bits(rng.uniform(0.5, 1.5, D).astype(np.float32))
+    wk_bits = workloads.f32_to_bf16_bits(rng.uniform(0.5, 1.5, D).astype(np.float32))
+    q, k, v = to_device(inp["q"], torch), to_device(inp["k"], torch), to_device(inp["v"], torch)
+    wq, wk = to_device(wq_bits, torch), to_device(wk_bits, torch)
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.n_q_heads, w.total_tokens), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def two_pass():
+        h3.qk_norm_rope(q, k, wq, wk, q_out=qo, k_out=ko, stream=stream)
+        h3.gqa_causal_fwd(qo, ko, v, softmax_scale=w.scale, out=o, lse=lse, stream=stream)
+
+    def fused():
+        h3.qk_norm_rope(None, k, None, wk, k_out=ko, stream=stream)
+        h3.gqa_causal_qnorm_rope_fwd(q, ko, v, q_norm_weight=wq, softmax_scale=w.scale, out=o,
+                                     lse=lse, stream=stream)
+
+    def timed(step):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    # alternate so both see the same clock; report the median of three rounds each
+    t2, t1 = [], []
+    for _ in range(3):
+        t2.append(timed(two_pass))
+        t1.append(timed(fused))
+    ms_two, ms_fused = float(np.median(t2)), float(np.median(t1))
+    flop = w.flop()
+    result = {
+        "metric": f"Q/K norm+RoPE + causal GQA fwd TFLOP/s (bf16), {w.name}",
+        "value": round(flop / (ms_fused * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_fused, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "total_tokens": w.total_tokens, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": D, "path": "qpro",
+                   "norm": "RMS, synthetic U(0.5,1.5) weights, eps 1e-6", "rope_theta": 1e6,
+                   "ms_two_pass": round(ms_two, 5), "ms_fused": round(ms_fused, 5),
+                   "fused_over_two_pass": round(ms_two / ms_fused, 4)},
+    }
+    if not args.no_check:
+        import oracle
+
+        fused()
+        torch.cuda.synchronize()
+        rq = workloads.f32_to_bf16_bits(oracle.qk_norm_rope(inp["q"], weight=wq_bits)
+                                        .astype(np.float32))
+        rk = workloads.f32_to_bf16_bits(oracle.qk_norm_rope(inp["k"], weight=wk_bits)
+                                        .astype(np.float32))
+        tokens = workloads.sample_tokens(w.seqlens, 8, seed=w.seed + 1000)
+        o_ref, lse_ref = oracle.gqa_causal(rq, rk, inp["v"], w.scale, tokens=tokens)
+        tok_t = torch.from_numpy(tokens).to("cuda")
+        o_s = o.index_select(0, tok_t).double().cpu().numpy()
+        l_s = lse.index_select(1, tok_t).double().cpu().numpy()
+        rel = float(np.linalg.norm(o_s - o_ref) / np.linalg.norm(o_ref))
+        mx = float(np.abs(o_s - o_ref).max())
+        lmx = float(np.abs(l_s - lse_ref).max())
+        result["oracle_match"] = {"tokens": int(len(tokens)), "rel_l2": rel, "max_abs": mx,
+                                  "lse_abs": lmx,
+                                  "pass": bool(rel <= 5e-3 and mx <= 2e-2 and lmx <= 1e-3)}
+    print(json.dumps(result), flush=True)
+
+
 def bench_pool(args, w, torch, h3):
     """Token pooling of a prompt of the workload's length: the issue's ~7500 reference-video
     tokens ([2300, 9800) of 10231) pooled by 4, C = 4096 synthetic embedding channels.
@@ -316,6 +402,12 @@ def main():
     inp = workloads.generate(w)
     if args.path == "prologue":
         bench_prologue(args, w, inp, torch, h3)
+        return
+    if args.path == "qpro":
+        if w.varlen or not w.causal:
+            print("bench.py: the qpro path takes one causal sequence", file=sys.stderr)
+            sys.exit(2)
+        bench_qpro(args, w, inp, torch, h3)
         return
     q, k, v = to_device(inp["q"], torch), to_device(inp["k"], torch), to_device(inp["v"], torch)
     o = (torch.empty((w.n_q_heads, w.total_tokens, w.head_dim), dtype=torch.bfloat16,

@@ -35,7 +35,8 @@ PROLOGUE_ROPE = 1                # flag of h3attn_qk_norm_rope
 
 EXPORTED = ("h3attn_gqa_causal_fwd", "h3attn_gqa_fwd", "h3attn_gqa_causal_varlen_fwd",
             "h3attn_gqa_causal_splitkv_fwd", "h3attn_gqa_causal_splitkv_workspace_bytes",
-            "h3attn_qk_norm_rope", "h3attn_pool_tokens", "h3attn_pool_tokens_out_len",
+            "h3attn_qk_norm_rope", "h3attn_gqa_causal_qnorm_rope_fwd", "h3attn_pool_tokens",
+            "h3attn_pool_tokens_out_len",
             "h3attn_status_string", "h3attn_version",
             "h3attn_lds_bytes")
 
@@ -78,6 +79,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         lib.h3attn_qk_norm_rope.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, f32, f32,
                                             vp, i32, vp]
         lib.h3attn_qk_norm_rope.restype = i32
+        lib.h3attn_gqa_causal_qnorm_rope_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                         f32, vp, f32, f32, vp, i32, vp]
+        lib.h3attn_gqa_causal_qnorm_rope_fwd.restype = i32
         lib.h3attn_pool_tokens.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp]
         lib.h3attn_pool_tokens.restype = i32
         lib.h3attn_pool_tokens_out_len.argtypes = [i32, i32, i32, i32]
@@ -221,29 +225,34 @@ def qk_norm_rope(q, k, q_norm_weight=None, k_norm_weight=None, eps: float = 1e-6
     """Q/K prologue (h3attn_qk_norm_rope): per-head RMS norm (when a weight is given) and
     rotate-half RoPE.  q [S,Hq,D], k [S,Hkv,D] bf16 on the GPU; weights bf16 [D];
     positions an int32 GPU tensor [S] (default: token index).  Returns (q_out, k_out);
-    pass q_out=q, k_out=k to work in place."""
+    pass q_out=q, k_out=k to work in place.  q=None transforms K only (q_out is None)."""
     import torch
 
     for name, t in (("q", q), ("k", k)):
+        if name == "q" and t is None:
+            continue
         if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 3 \
                 or not t.is_contiguous() or t.device.type != "cuda":
             raise ValueError(f"h3attn: {name} must be a contiguous bf16 [S, H, D] GPU tensor")
-    S, Hq, D = q.shape
-    if k.shape[0] != S or k.shape[2] != D:
-        raise ValueError("h3attn: q [S,Hq,D] and k [S,Hkv,D] must agree on S and D")
-    Hkv = k.shape[1]
-    q_out = torch.empty_like(q) if q_out is None else q_out
+    S, Hkv, D = k.shape
+    Hq = 0
+    if q is not None:
+        Hq = q.shape[1]
+        if q.shape[0] != S or q.shape[2] != D:
+            raise ValueError("h3attn: q [S,Hq,D] and k [S,Hkv,D] must agree on S and D")
+        q_out = torch.empty_like(q) if q_out is None else q_out
     k_out = torch.empty_like(k) if k_out is None else k_out
-    for name, t, ref in (("q_out", q_out, q), ("k_out", k_out, k)):
+    pairs = (("k_out", k_out, k),) if q is None else (("q_out", q_out, q), ("k_out", k_out, k))
+    for name, t, ref in pairs:
         if t.shape != ref.shape or t.dtype != torch.bfloat16 or not t.is_contiguous() \
                 or t.device != ref.device:
             raise ValueError(f"h3attn: {name} must be a contiguous bf16 tensor shaped like its input")
     for name, t in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
-        if t is not None and (t.dtype != torch.bfloat16 or t.numel() != D or t.device != q.device
+        if t is not None and (t.dtype != torch.bfloat16 or t.numel() != D or t.device != k.device
                               or not t.is_contiguous()):
             raise ValueError(f"h3attn: {name} must be a contiguous bf16 GPU tensor of D values")
     if positions is not None and (positions.dtype != torch.int32 or positions.numel() != S
-                                  or positions.device != q.device
+                                  or positions.device != k.device
                                   or not positions.is_contiguous()):
         raise ValueError("h3attn: positions must be a contiguous int32 GPU tensor of S values")
 
@@ -251,11 +260,44 @@ def qk_norm_rope(q, k, q_norm_weight=None, k_norm_weight=None, eps: float = 1e-6
         return None if t is None else t.data_ptr()
 
     rc = load_library().h3attn_qk_norm_rope(
-        q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), S, Hq, Hkv, D,
+        ptr(q), k.data_ptr(), ptr(q_out), k_out.data_ptr(), S, Hq, Hkv, D,
         ptr(q_norm_weight), ptr(k_norm_weight), float(eps), float(rope_theta), ptr(positions),
-        PROLOGUE_ROPE if rope else 0, _stream_handle(stream, q.device))
+        PROLOGUE_ROPE if rope else 0, _stream_handle(stream, k.device))
     _check(rc)
     return q_out, k_out
+
+
+def gqa_causal_qnorm_rope_fwd(q, k, v, q_norm_weight=None, eps: float = 1e-6, rope: bool = True,
+                              rope_theta: float = 1e6, positions=None,
+                              softmax_scale: float | None = None, out=None, lse=None,
+                              return_lse: bool = True, stream=None):
+    """Causal GQA forward with Q's RMS norm and RoPE applied inside the attention kernel
+    (h3attn_gqa_causal_qnorm_rope_fwd).  q [S,Hq,D], k and v [S,Hkv,D] bf16 on the GPU; k
+    already normalised and rotated (qk_norm_rope(None, k, ...)).  Returns (o, lse)."""
+    import torch
+
+    _check_tensors(q, k, v)
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if q_norm_weight is not None and (q_norm_weight.dtype != torch.bfloat16
+                                      or q_norm_weight.numel() != D
+                                      or q_norm_weight.device != q.device
+                                      or not q_norm_weight.is_contiguous()):
+        raise ValueError("h3attn: q_norm_weight must be a contiguous bf16 GPU tensor of D values")
+    if positions is not None and (positions.dtype != torch.int32 or positions.numel() != S
+                                  or positions.device != q.device
+                                  or not positions.is_contiguous()):
+        raise ValueError("h3attn: positions must be a contiguous int32 GPU tensor of S values")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    out, lse = _outputs(q, out, lse, return_lse)
+    rc = load_library().h3attn_gqa_causal_qnorm_rope_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, S, Hq, Hkv, D, scale,
+        None if q_norm_weight is None else q_norm_weight.data_ptr(), float(eps),
+        float(rope_theta), None if positions is None else positions.data_ptr(),
+        PROLOGUE_ROPE if rope else 0, _stream_handle(stream, q.device))
+    _check(rc)
+    return out, lse
 
 
 def pool_tokens_out_len(T: int, begin: int, end: int, factor: int) -> int:
@@ -360,4 +402,5 @@ def gqa_causal_splitkv_fwd(q, k, v, num_splits: int, softmax_scale: float | None
 __all__ = ["gqa_causal_fwd", "gqa_fwd", "gqa_causal_varlen_fwd", "gqa_causal_splitkv_fwd",
            "splitkv_workspace_bytes", "status_string", "version", "lds_bytes", "load_library",
            "H3AttnError", "LIBRARY", "EXPORTED", "MAX_SPLITS", "NONCAUSAL", "O_HEAD_MAJOR",
-           "qk_norm_rope", "PROLOGUE_ROPE", "pool_tokens", "pool_tokens_out_len"]
+           "qk_norm_rope", "gqa_causal_qnorm_rope_fwd", "PROLOGUE_ROPE", "pool_tokens",
+           "pool_tokens_out_len"]

@@ -80,6 +80,45 @@ int dispatch(int D, int G, const FwdParams& p, hipStream_t stream) {
   return H3ATTN_ERR_UNSUPPORTED;
 }
 
+// The causal forward with the Q prologue done in the kernel (fixed-length calls only).  Its
+// LDS holds the K/V ring plus a cos/sin table of the block's tokens: TOK_WG x D/2 x 8 bytes.
+template <int D, int G>
+int launch_qpro(const FwdParams& p, const h3attn::QproParams& qp, hipStream_t stream) {
+  using C = Cfg<D, G>;
+  static_assert(C::LDS_BYTES + C::TOK_WG * (D / 2) * 8 <= 160 * 1024, "LDS");
+  FwdParams pp = p;
+  pp.n_qblk = (p.seq_len + C::TOK_WG - 1) / C::TOK_WG;
+  const long long blocks = (long long)pp.n_qblk * p.hkv;
+  if (blocks == 0) return H3ATTN_OK;
+  if (blocks > 0x7fffffffLL) return H3ATTN_ERR_SHAPE;
+  hipLaunchKernelGGL((h3attn::gqa_causal_qpro_fwd_kernel<C>), dim3((unsigned)blocks),
+                     dim3(C::THREADS), 0, stream, pp, qp);
+  return hipGetLastError() == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
+}
+
+// (D, G) pairs with a qpro instance: at D = 128 and G = 1 the table (256 tokens) would not
+// fit beside the K/V ring.
+bool qpro_supported(int D, int G) { return D == 64 || G != 1; }
+
+int dispatch_qpro(int D, int G, const FwdParams& p, const h3attn::QproParams& qp,
+                  hipStream_t stream) {
+  if (D == 128) {
+    switch (G) {
+      case 2: return launch_qpro<128, 2>(p, qp, stream);
+      case 4: return launch_qpro<128, 4>(p, qp, stream);
+      case 8: return launch_qpro<128, 8>(p, qp, stream);
+    }
+  } else if (D == 64) {
+    switch (G) {
+      case 1: return launch_qpro<64, 1>(p, qp, stream);
+      case 2: return launch_qpro<64, 2>(p, qp, stream);
+      case 4: return launch_qpro<64, 4>(p, qp, stream);
+      case 8: return launch_qpro<64, 8>(p, qp, stream);
+    }
+  }
+  return H3ATTN_ERR_UNSUPPORTED;
+}
+
 // Split-KV: the split instance of the attention kernel writes per-split partials to the
 // workspace, then the merge kernel combines them into o and lse (same stream, in order).
 template <int D, int G>
@@ -240,12 +279,51 @@ int h3attn_gqa_fwd(const void* q, const void* k, const void* v, void* o, float* 
                                     : dispatch<false, true>(D, Hq / Hkv, p, st);
 }
 
+int h3attn_gqa_causal_qnorm_rope_fwd(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, int S, int Hq, int Hkv, int D,
+                                     float softmax_scale, const void* q_norm_weight, float eps,
+                                     float rope_theta, const int32_t* positions, int flags,
+                                     void* hip_stream) {
+  const int rc = check_common(q, k, v, o, lse, S, Hq, Hkv, D, softmax_scale);
+  if (rc != H3ATTN_OK) return rc;
+  if ((flags & ~H3ATTN_PROLOGUE_ROPE) != 0 || !qpro_supported(D, Hq / Hkv))
+    return H3ATTN_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(q_norm_weight) & 15u) != 0 ||
+      (reinterpret_cast<uintptr_t>(positions) & 3u) != 0)
+    return H3ATTN_ERR_ALIGN;
+  const bool rope = (flags & H3ATTN_PROLOGUE_ROPE) != 0;
+  if (q_norm_weight && (!std::isfinite(eps) || eps < 0.0f)) return H3ATTN_ERR_SCALE;
+  if (rope && (!std::isfinite(rope_theta) || !(rope_theta > 0.0f))) return H3ATTN_ERR_SCALE;
+  if (S == 0) return H3ATTN_OK;
+  if (!device_ok()) return H3ATTN_ERR_DEVICE;
+  FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.cu_seqlens = nullptr;
+  p.seq_len = S;
+  p.total_tokens = S;
+  p.num_seqs = 1;
+  p.hq = Hq;
+  p.hkv = Hkv;
+  p.scale_log2 = softmax_scale * kLog2e;
+  h3attn::QproParams qp{};
+  qp.q_weight = static_cast<const uint16_t*>(q_norm_weight);
+  qp.positions = positions;
+  qp.inv_freq_step = std::pow((double)rope_theta, -2.0 / (double)D);
+  qp.q_eps = eps;
+  qp.rope = rope ? 1 : 0;
+  return dispatch_qpro(D, Hq / Hkv, p, qp, static_cast<hipStream_t>(hip_stream));
+}
+
 int h3attn_qk_norm_rope(const void* q, const void* k, void* q_out, void* k_out, int S, int Hq,
                         int Hkv, int D, const void* q_norm_weight, const void* k_norm_weight,
                         float eps, float rope_theta, const int32_t* positions, int flags,
                         void* hip_stream) {
-  if (S > 0 && (!q || !k || !q_out || !k_out)) return H3ATTN_ERR_NULL;
-  if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return H3ATTN_ERR_SHAPE;
+  if (S > 0 && (!k || !k_out || (Hq > 0 && (!q || !q_out)))) return H3ATTN_ERR_NULL;
+  if (S < 0 || Hq < 0 || Hkv <= 0 || D <= 0) return H3ATTN_ERR_SHAPE;
   if ((long long)S * (long long)(Hq > Hkv ? Hq : Hkv) * (long long)D >= (1LL << 31))
     return H3ATTN_ERR_SHAPE;
   if ((D != 64 && D != 128) || (flags & ~H3ATTN_PROLOGUE_ROPE) != 0)
@@ -375,7 +453,7 @@ const char* h3attn_status_string(int status) {
   }
 }
 
-int h3attn_version(void) { return 200; }
+int h3attn_version(void) { return 300; }
 
 int h3attn_lds_bytes(int D, int G) {
   if (D == 128) {

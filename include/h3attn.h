@@ -180,6 +180,8 @@ H3ATTN_API size_t h3attn_gqa_causal_splitkv_workspace_bytes(int S, int Hq, int D
  *       z_i = y_i cos a_i - y_{i+D/2} sin a_i,   z_{i+D/2} = y_{i+D/2} cos a_i + y_i sin a_i
  * in fp32 (angles, cos and sin in fp64) with one bf16 rounding per output element.
  * q_out / k_out have q's / k's shapes and may equal q / k (in place).  D in {64, 128}.
+ * Hq may be 0 (K only, as before h3attn_gqa_causal_qnorm_rope_fwd); q and q_out may then
+ * be NULL.
  * Pointers: tensors and weights 16-byte aligned, positions 4-byte aligned,
  * all DEVICE memory.  eps must be finite and >= 0 when a weight is given (a row of
  * zeros with eps = 0 gives NaN, as the definition does); rope_theta finite and > 0 when
@@ -190,6 +192,30 @@ H3ATTN_API int h3attn_qk_norm_rope(const void* q, const void* k, void* q_out, vo
                                    int Hq, int Hkv, int D, const void* q_norm_weight,
                                    const void* k_norm_weight, float eps, float rope_theta,
                                    const int32_t* positions, int flags, void* hip_stream);
+
+/*
+ * Fixed-length causal GQA forward whose Q goes through the Q half of the prologue above
+ * (the README's fused QK-normalization / RoPE step) inside the attention kernel, as it is
+ * loaded: Q is read from HBM once and no normalised copy is written.  K must already be
+ * normalised and rotated, e.g. by h3attn_qk_norm_rope with Hq = 0.
+ *
+ *   q [S, Hq, D], k and v [S, Hkv, D] bf16 -> o [S, Hq, D] bf16, lse [Hq, S] fp32 (or NULL)
+ *   q_norm_weight  [D] bf16 or NULL (no norm); eps as in h3attn_qk_norm_rope
+ *   flags          H3ATTN_PROLOGUE_ROPE: rotary embedding with rope_theta and positions
+ *                  (int32 [S] or NULL: the token index), as in h3attn_qk_norm_rope
+ *
+ * The result is the causal forward of h3attn_gqa_causal_fwd applied to the bf16 output
+ * q_out that h3attn_qk_norm_rope would produce, up to rounding: the angles are reduced
+ * modulo 2 pi in fp64 and their cos / sin taken in fp32, and the row's sum of squares is
+ * added in another order.  Checks and errors as h3attn_gqa_causal_fwd and
+ * h3attn_qk_norm_rope; D = 128 with Hq == Hkv is not offered (H3ATTN_ERR_UNSUPPORTED).
+ */
+H3ATTN_API int h3attn_gqa_causal_qnorm_rope_fwd(const void* q, const void* k, const void* v,
+                                                void* o, float* lse, int S, int Hq, int Hkv,
+                                                int D, float softmax_scale,
+                                                const void* q_norm_weight, float eps,
+                                                float rope_theta, const int32_t* positions,
+                                                int flags, void* hip_stream);
 
 /*
  * Reference-video token pooling, the second fix direction of the issue ("Suggested fix

@@ -11,7 +11,9 @@ sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
 
-KERNEL = os.path.join("causal_grouped_query_amd", "csrc", "gqa_fwd_kernel.hpp")
+CSRC = os.path.join("causal_grouped_query_amd", "csrc")
+KERNEL = os.path.join(CSRC, "gqa_fwd_kernel.hpp")
+BODY = os.path.join(CSRC, "gqa_fwd_body.inc")
 TRAFFIC = os.path.join("profiles", "gqa_causal_fwd_s10231_hbm_traffic.txt")
 
 
@@ -24,8 +26,9 @@ def test_more_than_one_gpu_is_refused():
 
 
 def _fake_tree(tmp_path, kernel_text: bytes, recorded_hash: str, nbytes: int = 123456):
-    (tmp_path / os.path.dirname(KERNEL)).mkdir(parents=True)
+    (tmp_path / CSRC).mkdir(parents=True)
     (tmp_path / KERNEL).write_bytes(kernel_text)
+    (tmp_path / BODY).write_bytes(b"")
     (tmp_path / "profiles").mkdir()
     (tmp_path / TRAFFIC).write_text(
         "header line\n"
@@ -44,8 +47,9 @@ def test_recorded_traffic_needs_the_measured_source(tmp_path, monkeypatch):
 
 def test_recorded_traffic_missing_or_malformed(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    (tmp_path / os.path.dirname(KERNEL)).mkdir(parents=True)
+    (tmp_path / CSRC).mkdir(parents=True)
     (tmp_path / KERNEL).write_bytes(b"x")
+    (tmp_path / BODY).write_bytes(b"y")
     assert bench.recorded_traffic() is None            # no record at all
     (tmp_path / "profiles").mkdir()
     (tmp_path / TRAFFIC).write_text("traffic_bytes_per_launch: 5\n")
@@ -55,8 +59,11 @@ def test_recorded_traffic_missing_or_malformed(tmp_path, monkeypatch):
 def test_committed_traffic_record_matches_committed_kernel():
     """The HBM traffic under profiles/ was taken on the kernel source in the tree, so the
     benchmark line reports it (a kernel change must come with a new counter run)."""
-    with open(os.path.join(ROOT, KERNEL), "rb") as f:
-        h = hashlib.sha256(f.read()).hexdigest()
+    hs = hashlib.sha256()
+    for path in (KERNEL, BODY):
+        with open(os.path.join(ROOT, path), "rb") as f:
+            hs.update(f.read())
+    h = hs.hexdigest()
     with open(os.path.join(ROOT, TRAFFIC)) as f:
         lines = [ln.split() for ln in f if ln.startswith("traffic_bytes_per_launch:")]
     assert lines, "no traffic record in the profile"
