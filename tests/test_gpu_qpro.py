@@ -71,6 +71,7 @@ CASES = [  # S, Hq, Hkv, D, seed, norm, rope, explicit positions
     (64, 4, 4, 64, 706, True, False, False),     # D = 64 MHA, norm only
     (333, 8, 2, 64, 707, True, True, True),      # D = 64, G = 4
     (260, 16, 2, 64, 708, True, True, False),    # D = 64, G = 8
+    (150, 16, 2, 128, 709, True, True, "far"),   # positions near 10^5 (fp64 angle reduction)
 ]
 
 
@@ -80,7 +81,9 @@ def test_qpro_small(lib, S, Hq, Hkv, D, seed, norm, rope, explicit):
     wq = _weights(seed + 1000, D) if norm else None
     wk = _weights(seed + 2000, D) if norm else None
     positions = None
-    if explicit:
+    if explicit == "far":
+        positions = (100000 - np.arange(S, dtype=np.int32) * 7).astype(np.int32)
+    elif explicit:
         positions = (np.arange(S, dtype=np.int32) * 3 + 5000).astype(np.int32)
     scale = workloads.default_scale(D)
     o, lse, kp = _run(lib, q, k, v, wq, wk, rope, positions, scale)
