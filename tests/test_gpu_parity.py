@@ -154,15 +154,22 @@ def test_causality_bit_identical(lib):
         assert np.array_equal(lb1[:, :t], to_f64(l2)[:, :t]), f"LSE rows < {t} changed"
 
 
-def test_varlen_equals_single_calls(lib):
+@pytest.mark.parametrize("Hq,Hkv,D,seed", [
+    (16, 2, 128, 140),   # G = 8
+    (8, 4, 128, 141),    # G = 2
+    (8, 8, 64, 142),     # G = 1
+    (16, 4, 64, 143),    # G = 4
+    (8, 1, 64, 144),     # G = 8
+])
+def test_varlen_equals_single_calls(lib, Hq, Hkv, D, seed):
     """A packed batch gives bit-identical results to one call per sequence,
-    including empty sequences and lengths that are not multiples of any tile."""
+    including empty sequences and lengths that are not multiples of any tile,
+    for the packed instance of each group size and head dim checked."""
     import torch
 
     lens = [130, 0, 1, 64, 517, 0, 33]
-    Hq, Hkv, D = 16, 2, 128
     T = sum(lens)
-    q, k, v = normal_inputs(140, T, Hq, Hkv, D)
+    q, k, v = normal_inputs(seed, T, Hq, Hkv, D)
     scale = workloads.default_scale(D)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     qd, kd, vd = to_device(q), to_device(k), to_device(v)
@@ -178,7 +185,7 @@ def test_varlen_equals_single_calls(lib):
         assert np.array_equal(ob[a:b], bits_of(o1)), f"sequence {s} differs"
         assert np.array_equal(lf[:, a:b], to_f64(l1)), f"sequence {s} LSE differs"
     o_ref, lse_ref = oracle.gqa_causal_varlen(q, k, v, cu, scale)
-    assert_close(to_f64(o), lf, o_ref, lse_ref, "varlen mixed lengths")
+    assert_close(to_f64(o), lf, o_ref, lse_ref, f"varlen mixed lengths {Hq}/{Hkv} D={D}")
 
 
 def test_deterministic_and_lse_optional(lib):
