@@ -16,6 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", "h3attn.hip")]
 HEADERS = [os.path.join(PKG, "csrc", "gqa_fwd_kernel.hpp"), os.path.join(PKG, "csrc", "gqa_fwd_body.inc"),
+           os.path.join(PKG, "csrc", "gqa_fwd_wide_kernel.hpp"), os.path.join(PKG, "csrc", "tile_phases.inc"),
            os.path.join(ROOT, "include", "h3attn.h")]
 LIBRARY = os.path.join(PKG, "libh3attn.so")
 ARCH = "gfx950"

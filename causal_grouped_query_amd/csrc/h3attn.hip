@@ -15,6 +15,7 @@
 #include <cstring>
 
 #include "gqa_fwd_kernel.hpp"
+#include "gqa_fwd_wide_kernel.hpp"
 #include "gqa_merge_kernel.hpp"
 #include "pool_tokens_kernel.hpp"
 #include "qk_prologue_kernel.hpp"
@@ -60,14 +61,27 @@ int launch(FwdParams p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
 }
 
+// Head dim 128: the wide kernel (4 waves of 64 query rows, gqa_fwd_wide_kernel.hpp).
+template <int G, bool VARLEN, bool CAUSAL>
+int launch_wide(FwdParams p, hipStream_t stream) {
+  using C = h3attn::WideConfig<128, G>;
+  p.n_qblk = (p.seq_len + C::TOK_WG - 1) / C::TOK_WG;
+  const long long blocks = (long long)p.n_qblk * p.hkv * p.num_seqs;
+  if (blocks == 0) return H3ATTN_OK;
+  if (blocks > 0x7fffffffLL) return H3ATTN_ERR_SHAPE;
+  hipLaunchKernelGGL((h3attn::gqa_fwd_wide_kernel<C, VARLEN, CAUSAL>), dim3((unsigned)blocks),
+                     dim3(C::THREADS), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
+}
+
 template <bool VARLEN, bool CAUSAL = true>
 int dispatch(int D, int G, const FwdParams& p, hipStream_t stream) {
   if (D == 128) {
     switch (G) {
-      case 1: return launch<128, 1, VARLEN, CAUSAL>(p, stream);
-      case 2: return launch<128, 2, VARLEN, CAUSAL>(p, stream);
-      case 4: return launch<128, 4, VARLEN, CAUSAL>(p, stream);
-      case 8: return launch<128, 8, VARLEN, CAUSAL>(p, stream);
+      case 1: return launch_wide<1, VARLEN, CAUSAL>(p, stream);
+      case 2: return launch_wide<2, VARLEN, CAUSAL>(p, stream);
+      case 4: return launch_wide<4, VARLEN, CAUSAL>(p, stream);
+      case 8: return launch_wide<8, VARLEN, CAUSAL>(p, stream);
     }
   } else if (D == 64) {
     switch (G) {
@@ -456,12 +470,12 @@ const char* h3attn_status_string(int status) {
 int h3attn_version(void) { return 300; }
 
 int h3attn_lds_bytes(int D, int G) {
-  if (D == 128) {
+  if (D == 128) {   // the wide kernel of the causal / packed / bidirectional calls
     switch (G) {
-      case 1: return Cfg<128, 1>::LDS_BYTES;
-      case 2: return Cfg<128, 2>::LDS_BYTES;
-      case 4: return Cfg<128, 4>::LDS_BYTES;
-      case 8: return Cfg<128, 8>::LDS_BYTES;
+      case 1: return h3attn::WideConfig<128, 1>::LDS_BYTES;
+      case 2: return h3attn::WideConfig<128, 2>::LDS_BYTES;
+      case 4: return h3attn::WideConfig<128, 4>::LDS_BYTES;
+      case 8: return h3attn::WideConfig<128, 8>::LDS_BYTES;
     }
   } else if (D == 64) {
     switch (G) {
