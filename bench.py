@@ -38,8 +38,10 @@ def log(msg: str) -> None:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # about 2.2 s timed after 0.45 s of warmup at S=10231: the shader clock and power
+    # readings are refreshed by the firmware about once a second
+    ap.add_argument("--steps", type=int, default=1500)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=workloads.PRIMARY,
                     choices=sorted(workloads.ALL_WORKLOADS))
     ap.add_argument("--path", default="fused",
@@ -75,34 +77,141 @@ def copy_probe(mib: int) -> None:
     print(json.dumps({"copy_probe_bytes": n}), flush=True)
 
 
-# the attention kernel's source (its statements and its launch configuration)
-KERNEL_SOURCES = ("gqa_fwd_kernel.hpp", "gqa_fwd_body.inc")
+# the benchmarked kernel's source: the head-dim-128 forward (its statements, its launch shape,
+# its generated phases, and the shared parameter block / helpers it includes)
+KERNEL_SOURCES = ("gqa_fwd_wide_kernel.hpp", "tile_phases.inc", "gqa_fwd_kernel.hpp")
+KERNEL_NAME = "gqa_fwd_wide_kernel<WideConfig<128, 8>, false, true>"
+# counter runs of that kernel on the benchmarked workload (trace, utilisation, HBM traffic)
+PROFILE = "gqa_fwd_wide_s10231.txt"
 
 
-def recorded_traffic():
-    """HBM bytes per launch recorded for the current kernel source, or None.
-
-    profiles/gqa_causal_fwd_s10231_hbm_traffic.txt holds a line
-    `traffic_bytes_per_launch: N source_sha256: H`; the figure applies only while the
-    attention kernel's source (csrc/gqa_fwd_kernel.hpp and csrc/gqa_fwd_body.inc, which also
-    fix its launch configuration), hashed in that order, is still H."""
+def kernel_source_hash() -> str:
+    """sha256 over the benchmarked kernel's source files, in KERNEL_SOURCES order."""
     import hashlib
 
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "causal_grouped_query_amd", "csrc", name), "rb") as f:
             h.update(f.read())
-    path = os.path.join(ROOT, "profiles", "gqa_causal_fwd_s10231_hbm_traffic.txt")
+    return h.hexdigest()
+
+
+def recorded(profile: str, key: str):
+    """A figure recorded in profiles/<profile> for the current kernel source, or None.
+
+    The file holds a line `<key>: VALUE source_sha256: H`; the figure applies only while the
+    kernel's source (KERNEL_SOURCES, hashed in that order) is still H."""
+    path = os.path.join(ROOT, "profiles", profile)
+    want = kernel_source_hash()
     try:
         with open(path) as f:
             for line in f:
-                if line.startswith("traffic_bytes_per_launch:"):
+                if line.startswith(key + ":"):
                     parts = line.split()
-                    if parts[3] == h.hexdigest():
-                        return int(parts[1])
+                    if parts[3] == want:
+                        return float(parts[1])
     except (OSError, IndexError, ValueError):
         pass
     return None
+
+
+def _int_or_none(x):
+    return None if x is None else int(x)
+
+
+class ClockSampler:
+    """Reads the shader (gfx) clock of every XCD and the socket power from amdsmi's
+    gpu_metrics on a thread while the launches run.  The firmware refreshes that table about
+    once a second (its system_clock_counter field changes then), so the reader polls every
+    few ms from the warmup on and keeps each refresh published inside the timed region
+    [begin, end] once.  Reports nothing (None) where amdsmi is missing or refuses."""
+
+    def __init__(self, period_s: float = 0.005):
+        self.period = period_s
+        self.samples = []   # (time, table counter, mean current gfxclk over XCDs, XCD clocks, W)
+        self.error = None
+        self.thread = None
+        self.stop_flag = False
+        self.begin = self.end = None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            self.amdsmi = amdsmi
+            self.handle = amdsmi.amdsmi_get_processor_handles()[0]
+            self._sample()          # fails here, not in the thread, if the call is refused
+        except Exception as e:      # noqa: BLE001 -- any failure just disables the sampler
+            self.amdsmi = None
+            self.error = f"{type(e).__name__}: {e}"[:200]
+
+    @staticmethod
+    def _valid(x):
+        return isinstance(x, int) and 0 < x < 100000
+
+    def _sample(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        clks = [c for c in (m.get("current_gfxclks") or []) if self._valid(c)]
+        if not clks and self._valid(m.get("current_gfxclk")):
+            clks = [m["current_gfxclk"]]
+        pw = m.get("current_socket_power")
+        self.samples.append((time.perf_counter(), m.get("system_clock_counter"),
+                             sum(clks) / len(clks) if clks else None, clks,
+                             pw if self._valid(pw) else None))
+
+    def _run(self):
+        while not self.stop_flag:
+            try:
+                self._sample()
+            except Exception as e:  # noqa: BLE001
+                self.error = f"{type(e).__name__}: {e}"[:200]
+                return
+            time.sleep(self.period)
+
+    def start(self):
+        if self.amdsmi is not None:
+            import threading
+
+            self.thread = threading.Thread(target=self._run, daemon=True)
+            self.thread.start()
+
+    def stop(self):
+        self.stop_flag = True
+        if self.thread is not None:
+            self.thread.join()
+        if self.amdsmi is not None:
+            try:
+                self.amdsmi.amdsmi_shut_down()
+            except Exception:       # noqa: BLE001
+                pass
+
+    def refreshes(self):
+        """The table refreshes first seen inside the timed region, one sample each."""
+        if self.begin is None:
+            return []
+        before = [smp[1] for smp in self.samples if smp[0] < self.begin]
+        seen = {before[-1]} if before else set()
+        out = []
+        for smp in self.samples:
+            if self.begin <= smp[0] <= self.end and smp[1] not in seen and smp[2] is not None:
+                seen.add(smp[1])
+                out.append(smp)
+        return out
+
+    def summary(self):
+        fresh = self.refreshes()
+        if not fresh:
+            return {"source": "amdsmi gpu_metrics", "mhz_mean": None,
+                    "error": self.error or "the metrics table was not refreshed inside the "
+                                           "timed region (run more steps)"}
+        c = np.array([smp[2] for smp in fresh])
+        out = {"source": "amdsmi gpu_metrics current_gfxclks (mean over the 8 XCDs), each "
+                         "firmware refresh (about 1/s) published inside the timed region",
+               "refreshes": int(len(c)), "mhz_mean": round(float(c.mean()), 1),
+               "xcd_mhz_last": fresh[-1][3]}
+        pw = [smp[4] for smp in fresh if smp[4] is not None]
+        if pw:
+            out["socket_power_w_mean"] = round(float(np.mean(pw)), 1)
+        return out
 
 
 def to_device(bits, torch):
@@ -433,6 +542,8 @@ def main():
         else:
             h3.gqa_causal_fwd(q, k, v, softmax_scale=w.scale, out=o, lse=lse, stream=stream)
 
+    sampler = ClockSampler()
+    sampler.start()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -442,13 +553,17 @@ def main():
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    t0 = sampler.begin = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
         step()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    sampler.end = time.perf_counter()
+    wall = sampler.end - t0
+    sampler.stop()
+    clock = sampler.summary()
+    log(f"shader clock during the timed launches: {clock}")
     per_launch = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms
     total_ms = starts[0].elapsed_time(ends[-1])
     ms_per_step = total_ms / args.steps
@@ -460,8 +575,20 @@ def main():
     avg_launch_ms = float(per_launch.mean())
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
 
+    primary = w.name == workloads.PRIMARY and args.path == "fused"
+    # MFMA peak at the clock the part actually ran: 256 CU x 4096 bf16 flop/clk x f
+    f_ghz = clock["mhz_mean"] / 1e3 if clock.get("mhz_mean") else None
+    clock["peak_at_clock_tflops"] = round(256 * 4096 * f_ghz / 1e3, 1) if f_ghz else None
+    clock["frac_at_clock"] = (round(achieved / clock["peak_at_clock_tflops"], 4)
+                              if f_ghz else None)
+    counter_ghz = recorded(PROFILE, "clock_ghz") if primary else None
+    clock["counter_clock_ghz"] = counter_ghz
+    clock["counter_clock_note"] = ("GRBM_GUI_ACTIVE per XCD / kernel duration, recorded in "
+                                   f"profiles/{PROFILE} for this source"
+                                   if counter_ghz else "no counter run of this source recorded")
+
     metric = METRIC
-    if w.name != workloads.PRIMARY or args.path != "fused":
+    if not primary:
         metric = (f"{'causal' if w.causal else 'bidirectional'} GQA fwd TFLOP/s (bf16), "
                   f"{w.name}, {args.path} path; oracle-match")
     result = {
@@ -498,12 +625,13 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": (recorded_traffic() if w.name == workloads.PRIMARY and args.path == "fused"
-                        else None),
-            "kernel": ("gqa_causal_fwd_kernel" if args.path == "fused" else
+            "traffic": _int_or_none(recorded(PROFILE, "traffic_bytes_per_launch")
+                                    if primary else None),
+            "kernel": (KERNEL_NAME if args.path == "fused" else
                        "gqa_causal_fwd_kernel<split> + merge_splits_kernel (one call, timed together)"),
             "avg_launch_ms": round(avg_launch_ms, 5),
             "algorithmic_flop_per_launch": flop,
+            "shader_clock": clock,
         },
     }
 

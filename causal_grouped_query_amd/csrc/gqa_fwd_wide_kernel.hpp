@@ -421,4 +421,19 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
   }
 }
 
+// Host side: one workgroup per (query block, KV head, sequence).  Returns the launch's HIP
+// error; hipSuccess without a launch for an empty grid, hipErrorInvalidConfiguration when the
+// grid would not fit the 32-bit x dimension.
+template <int G, bool VARLEN, bool CAUSAL>
+inline hipError_t launch_gqa_fwd_wide(FwdParams p, hipStream_t stream) {
+  using C = WideConfig<128, G>;
+  p.n_qblk = (p.seq_len + C::TOK_WG - 1) / C::TOK_WG;
+  const long long blocks = (long long)p.n_qblk * p.hkv * p.num_seqs;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((gqa_fwd_wide_kernel<C, VARLEN, CAUSAL>), dim3((unsigned)blocks),
+                     dim3(C::THREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace h3attn

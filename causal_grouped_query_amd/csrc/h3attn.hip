@@ -61,17 +61,13 @@ int launch(FwdParams p, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
 }
 
-// Head dim 128: the wide kernel (4 waves of 64 query rows, gqa_fwd_wide_kernel.hpp).
+// Head dim 128: the wide kernel (4 waves of 64 query rows, gqa_fwd_wide_kernel.hpp, which
+// also fixes its launch shape).
 template <int G, bool VARLEN, bool CAUSAL>
-int launch_wide(FwdParams p, hipStream_t stream) {
-  using C = h3attn::WideConfig<128, G>;
-  p.n_qblk = (p.seq_len + C::TOK_WG - 1) / C::TOK_WG;
-  const long long blocks = (long long)p.n_qblk * p.hkv * p.num_seqs;
-  if (blocks == 0) return H3ATTN_OK;
-  if (blocks > 0x7fffffffLL) return H3ATTN_ERR_SHAPE;
-  hipLaunchKernelGGL((h3attn::gqa_fwd_wide_kernel<C, VARLEN, CAUSAL>), dim3((unsigned)blocks),
-                     dim3(C::THREADS), 0, stream, p);
-  return hipGetLastError() == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
+int launch_wide(const FwdParams& p, hipStream_t stream) {
+  const hipError_t e = h3attn::launch_gqa_fwd_wide<G, VARLEN, CAUSAL>(p, stream);
+  if (e == hipErrorInvalidConfiguration) return H3ATTN_ERR_SHAPE;
+  return e == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
 }
 
 template <bool VARLEN, bool CAUSAL = true>
