@@ -5,8 +5,9 @@ CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
 with the HIP library in ``causal_grouped_query_amd`` and imports nothing from
 it; the product never imports this package.
 
-The arithmetic lives in ``oracle.c`` (plain C, double precision, one query
-row at a time).  This module only compiles it with gcc, loads it with ctypes
+The arithmetic lives in ``oracle.c`` (plain C, double precision, each query
+row on its own; the rows of the heads that share a KV head are evaluated
+together, which reads each key row once for them and changes no sum).  This module only compiles it with gcc, loads it with ctypes
 and marshals numpy arrays.  Inputs are bf16 bit patterns: ``numpy.uint16`` /
 ``int16`` arrays, or CPU ``torch.bfloat16`` tensors.
 
@@ -30,7 +31,7 @@ SOURCE = os.path.join(HERE, "oracle.c")
 LIBRARY = os.path.join(HERE, "liboracle.so")
 
 # Plain, unreordered IEEE double arithmetic: no fast-math, no FMA contraction.
-CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+CFLAGS = ["-O3", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
           "-fno-fast-math", "-Wall", "-Wextra"]
 
 

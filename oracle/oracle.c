@@ -11,8 +11,8 @@
  * text encoder's bf16 causal GQA, which forms, for every query token, the
  * causal attention score row over all earlier tokens and takes its softmax.
  * The tiled scheme that the same section proposes is only a faster way to the
- * same numbers, so this oracle writes the plain definition out, one query row
- * at a time, in double precision:
+ * same numbers, so this oracle writes the plain definition out, query row by
+ * query row, in double precision:
  *
  *   g        = h / G,  G = Hq / Hkv       (heads g*G .. g*G+G-1 share KV head g)
  *   x_j      = scale * sum_d Q[i,h,d] * K[j,g,d]      for j = 0 .. i (local)
@@ -53,9 +53,10 @@
  *     z_{i+D/2} = y_{i+D/2} * cos(a_i) + y_i * sin(a_i)
  * either step optional, all in double.
  *
- * Parallelism: (token, head) items are independent; OpenMP spreads them over
- * threads.  This changes no arithmetic: each item's sums run in the same order
- * whatever the thread count.
+ * Parallelism: (token, KV head) items are independent; OpenMP spreads them
+ * over threads.  One item evaluates the G query heads that share the KV head,
+ * reading each key and value row once for all G; each head's sums still run
+ * in the order the definition above writes them, whatever the thread count.
  */
 #include <math.h>
 #include <stdint.h>
@@ -72,42 +73,69 @@ static double bf16_bits_to_double(uint16_t bits) {
   return (double)f;
 }
 
-/* Attention of one query row over keys [first_key, last_key] (packed token
- * indices, inclusive), i.e. the causal prefix of its own sequence.  Writes
- * D doubles to out_o and returns the log-sum-exp.  scores: caller scratch of
- * at least (last_key - first_key + 1) doubles. */
-static double attend_one_row(const uint16_t* q_row,      /* D values of Q[i,h,:] */
-                             const uint16_t* k, const uint16_t* v,
-                             int64_t kv_token_stride,     /* Hkv * D */
-                             int64_t g, int64_t D, double scale,
-                             int64_t first_key, int64_t last_key,
-                             double* scores, double* out_o) {
+/* Attention of the G query heads h = g*G .. g*G+G-1 of one query token over
+ * keys [first_key, last_key] (packed token indices, inclusive), i.e. the causal
+ * prefix of its own sequence.  The G heads share KV head g, so each key row is
+ * read once for all of them; every head's arithmetic is the plain definition
+ * on its own, sums in key (or dimension) order exactly as for a single row:
+ *   dot  = ((q_0 k_0 + q_1 k_1) + q_2 k_2) + ...        (d = 0, 1, ..)
+ *   m    = max over keys, l = sum_t exp(x_t - m)        (t = 0, 1, ..)
+ *   o[d] = sum_t (exp(x_t - m) / l) v_t[d]              (t = 0, 1, ..)
+ * q_rows: the G rows Q[pos, g*G + hh, :] (D values each, stride D).
+ * Writes G rows of D doubles to out_o (stride o_stride) and G log-sum-exps to
+ * out_lse (stride lse_stride).  scores: caller scratch of at least
+ * G * (last_key - first_key + 1) doubles; dot, mx, sum: scratch of G doubles
+ * each; qt: G * D doubles; vd: D doubles. */
+static void attend_group(const uint16_t* q_rows, int64_t G,
+                         const uint16_t* k, const uint16_t* v,
+                         int64_t kv_token_stride,     /* Hkv * D */
+                         int64_t g, int64_t D, double scale,
+                         int64_t first_key, int64_t last_key,
+                         double* scores, double* dot, double* qt, double* mx, double* sum,
+                         double* vd,
+                         double* out_o, int64_t o_stride,
+                         double* out_lse, int64_t lse_stride) {
   const int64_t n = last_key - first_key + 1;
 
-  /* scores of the causal row */
+  /* the G query rows decoded once, dimension-major: qt[d * G + hh] */
+  for (int64_t hh = 0; hh < G; ++hh)
+    for (int64_t d = 0; d < D; ++d) qt[d * G + hh] = bf16_bits_to_double(q_rows[hh * D + d]);
+
+  /* scores of the causal rows: scores[hh * n + t] */
   for (int64_t t = 0; t < n; ++t) {
     const uint16_t* k_row = k + (first_key + t) * kv_token_stride + g * D;
-    double dot = 0.0;
-    for (int64_t d = 0; d < D; ++d)
-      dot += bf16_bits_to_double(q_row[d]) * bf16_bits_to_double(k_row[d]);
-    scores[t] = scale * dot;
+    for (int64_t hh = 0; hh < G; ++hh) dot[hh] = 0.0;
+    for (int64_t d = 0; d < D; ++d) {
+      const double kd = bf16_bits_to_double(k_row[d]);
+      for (int64_t hh = 0; hh < G; ++hh) dot[hh] += qt[d * G + hh] * kd;
+    }
+    for (int64_t hh = 0; hh < G; ++hh) scores[hh * n + t] = scale * dot[hh];
   }
 
-  /* max, then the sum of shifted exponentials */
-  double m = scores[0];
-  for (int64_t t = 1; t < n; ++t)
-    if (scores[t] > m) m = scores[t];
-  double l = 0.0;
-  for (int64_t t = 0; t < n; ++t) l += exp(scores[t] - m);
+  /* per head: the max, then the sum of shifted exponentials */
+  for (int64_t hh = 0; hh < G; ++hh) {
+    const double* x = scores + hh * n;
+    double m = x[0];
+    for (int64_t t = 1; t < n; ++t)
+      if (x[t] > m) m = x[t];
+    double l = 0.0;
+    for (int64_t t = 0; t < n; ++t) l += exp(x[t] - m);
+    mx[hh] = m;
+    sum[hh] = l;
+    for (int64_t d = 0; d < D; ++d) out_o[hh * o_stride + d] = 0.0;
+  }
 
-  /* probability-weighted sum of the value rows */
-  for (int64_t d = 0; d < D; ++d) out_o[d] = 0.0;
+  /* probability-weighted sums of the value rows, each value row decoded once */
   for (int64_t t = 0; t < n; ++t) {
-    const double p = exp(scores[t] - m) / l;
     const uint16_t* v_row = v + (first_key + t) * kv_token_stride + g * D;
-    for (int64_t d = 0; d < D; ++d) out_o[d] += p * bf16_bits_to_double(v_row[d]);
+    for (int64_t d = 0; d < D; ++d) vd[d] = bf16_bits_to_double(v_row[d]);
+    for (int64_t hh = 0; hh < G; ++hh) {
+      const double p = exp(scores[hh * n + t] - mx[hh]) / sum[hh];
+      double* o = out_o + hh * o_stride;
+      for (int64_t d = 0; d < D; ++d) o[d] += p * vd[d];
+    }
   }
-  return m + log(l);
+  for (int64_t hh = 0; hh < G; ++hh) out_lse[hh * lse_stride] = mx[hh] + log(sum[hh]);
 }
 
 /*
@@ -137,7 +165,7 @@ int oracle_gqa_causal_varlen(const uint16_t* q, const uint16_t* k, const uint16_
 
   const int64_t G = Hq / Hkv;
   const double scale = (double)scale_f32;
-  const int64_t n_items = ntok * Hq;
+  const int64_t n_items = ntok * Hkv;
   int status = 0;
 
 #ifdef _OPENMP
@@ -151,7 +179,7 @@ int oracle_gqa_causal_varlen(const uint16_t* q, const uint16_t* k, const uint16_
     int64_t longest = 0;
     for (int64_t s = 0; s < num_seqs; ++s)
       if (cu_seqlens[s + 1] - cu_seqlens[s] > longest) longest = cu_seqlens[s + 1] - cu_seqlens[s];
-    double* scores = (double*)malloc(sizeof(double) * (size_t)(longest > 0 ? longest : 1));
+    double* scores = (double*)malloc(sizeof(double) * (size_t)(G * (longest > 0 ? longest : 1) + 3 * G + G * D + D));
     if (!scores) {
 #pragma omp atomic write
       status = -5;
@@ -159,17 +187,17 @@ int oracle_gqa_causal_varlen(const uint16_t* q, const uint16_t* k, const uint16_
 #pragma omp for schedule(dynamic, 1)
     for (int64_t item = 0; item < n_items; ++item) {
       if (!scores) continue;
-      const int64_t ti = item / Hq;
-      const int64_t h = item % Hq;
+      const int64_t ti = item / Hkv;
+      const int64_t g = item % Hkv;
       const int64_t pos = tokens[ti];
       /* the sequence holding this packed position */
       int64_t s = 0;
       while (!(cu_seqlens[s] <= pos && pos < cu_seqlens[s + 1])) ++s;
-      const int64_t g = h / G;
-      const uint16_t* q_row = q + (pos * Hq + h) * D;
-      lse_out[h * ntok + ti] =
-          attend_one_row(q_row, k, v, Hkv * D, g, D, scale, cu_seqlens[s], pos, scores,
-                         o_out + (ti * Hq + h) * D);
+      const int64_t h0 = g * G;
+      attend_group(q + (pos * Hq + h0) * D, G, k, v, Hkv * D, g, D, scale, cu_seqlens[s], pos,
+                   scores + 3 * G + G * D + D, scores, scores + G, scores + G + G * D,
+                   scores + 2 * G + G * D, scores + 3 * G + G * D, o_out + (ti * Hq + h0) * D, D,
+                   lse_out + h0 * ntok + ti, ntok);
     }
     free(scores);
   }
@@ -204,7 +232,7 @@ int oracle_gqa_causal_keyrange(const uint16_t* q, const uint16_t* k, const uint1
 
   const int64_t G = Hq / Hkv;
   const double scale = (double)scale_f32;
-  const int64_t n_items = ntok * Hq;
+  const int64_t n_items = ntok * Hkv;
   int status = 0;
 
 #ifdef _OPENMP
@@ -215,7 +243,7 @@ int oracle_gqa_causal_keyrange(const uint16_t* q, const uint16_t* k, const uint1
 
 #pragma omp parallel
   {
-    double* scores = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    double* scores = (double*)malloc(sizeof(double) * (size_t)(G * (S > 0 ? S : 1) + 3 * G + G * D + D));
     if (!scores) {
 #pragma omp atomic write
       status = -5;
@@ -223,20 +251,24 @@ int oracle_gqa_causal_keyrange(const uint16_t* q, const uint16_t* k, const uint1
 #pragma omp for schedule(dynamic, 1)
     for (int64_t item = 0; item < n_items; ++item) {
       if (!scores) continue;
-      const int64_t ti = item / Hq;
-      const int64_t h = item % Hq;
+      const int64_t ti = item / Hkv;
+      const int64_t g = item % Hkv;
       const int64_t pos = tokens[ti];
-      const int64_t g = h / G;
+      const int64_t h0 = g * G;
       const int64_t first = key_begin > 0 ? key_begin : 0;
       const int64_t last = (key_end - 1 < pos) ? key_end - 1 : pos;
-      double* o_row = o_out + (ti * Hq + h) * D;
       if (first > last) {
-        for (int64_t d = 0; d < D; ++d) o_row[d] = 0.0;
-        lse_out[h * ntok + ti] = -INFINITY;
+        for (int64_t hh = 0; hh < G; ++hh) {
+          double* o_row = o_out + (ti * Hq + h0 + hh) * D;
+          for (int64_t d = 0; d < D; ++d) o_row[d] = 0.0;
+          lse_out[(h0 + hh) * ntok + ti] = -INFINITY;
+        }
         continue;
       }
-      lse_out[h * ntok + ti] = attend_one_row(q + (pos * Hq + h) * D, k, v, Hkv * D, g, D,
-                                              scale, first, last, scores, o_row);
+      attend_group(q + (pos * Hq + h0) * D, G, k, v, Hkv * D, g, D, scale, first, last,
+                   scores + 3 * G + G * D + D, scores, scores + G, scores + G + G * D,
+                   scores + 2 * G + G * D, scores + 3 * G + G * D, o_out + (ti * Hq + h0) * D, D,
+                   lse_out + h0 * ntok + ti, ntok);
     }
     free(scores);
   }
@@ -258,7 +290,7 @@ int oracle_gqa_bidirectional(const uint16_t* q, const uint16_t* k, const uint16_
 
   const int64_t G = Hq / Hkv;
   const double scale = (double)scale_f32;
-  const int64_t n_items = ntok * Hq;
+  const int64_t n_items = ntok * Hkv;
   int status = 0;
 
 #ifdef _OPENMP
@@ -269,7 +301,7 @@ int oracle_gqa_bidirectional(const uint16_t* q, const uint16_t* k, const uint16_
 
 #pragma omp parallel
   {
-    double* scores = (double*)malloc(sizeof(double) * (size_t)S);
+    double* scores = (double*)malloc(sizeof(double) * (size_t)(G * S + 3 * G + G * D + D));
     if (!scores) {
 #pragma omp atomic write
       status = -5;
@@ -277,13 +309,14 @@ int oracle_gqa_bidirectional(const uint16_t* q, const uint16_t* k, const uint16_
 #pragma omp for schedule(dynamic, 1)
     for (int64_t item = 0; item < n_items; ++item) {
       if (!scores) continue;
-      const int64_t ti = item / Hq;
-      const int64_t h = item % Hq;
+      const int64_t ti = item / Hkv;
+      const int64_t g = item % Hkv;
       const int64_t pos = tokens[ti];
-      const int64_t g = h / G;
-      lse_out[h * ntok + ti] = attend_one_row(q + (pos * Hq + h) * D, k, v, Hkv * D, g, D,
-                                              scale, 0, S - 1, scores,
-                                              o_out + (ti * Hq + h) * D);
+      const int64_t h0 = g * G;
+      attend_group(q + (pos * Hq + h0) * D, G, k, v, Hkv * D, g, D, scale, 0, S - 1,
+                   scores + 3 * G + G * D + D, scores, scores + G, scores + G + G * D,
+                   scores + 2 * G + G * D, scores + 3 * G + G * D, o_out + (ti * Hq + h0) * D, D,
+                   lse_out + h0 * ntok + ti, ntok);
     }
     free(scores);
   }

@@ -13,29 +13,34 @@ import oracle
 from oracle_pins import ALL_PINS
 
 MUTANTS = {
-    "interleaved_head_groups": ("const int64_t g = h / G;", "const int64_t g = h % Hkv;"),
+    # a query-head group read against the KV head of its first head's interleaved index
+    "interleaved_head_groups": ("Hkv * D, g, D, scale", "Hkv * D, (g * G) % Hkv, D, scale"),
     "diagonal_excluded": ("const int64_t n = last_key - first_key + 1;",
                           "const int64_t n = last_key - first_key;"),
-    "scale_dropped": ("scores[t] = scale * dot;", "scores[t] = dot;"),
-    "score_sign_flipped": ("scores[t] = scale * dot;", "scores[t] = -scale * dot;"),
-    "not_normalised": ("const double p = exp(scores[t] - m) / l;",
-                       "const double p = exp(scores[t] - m);"),
-    "lse_without_max": ("return m + log(l);", "return log(l);"),
+    "scale_dropped": ("scores[hh * n + t] = scale * dot[hh];", "scores[hh * n + t] = dot[hh];"),
+    "score_sign_flipped": ("scores[hh * n + t] = scale * dot[hh];",
+                           "scores[hh * n + t] = -scale * dot[hh];"),
+    "not_normalised": ("const double p = exp(scores[hh * n + t] - mx[hh]) / sum[hh];",
+                       "const double p = exp(scores[hh * n + t] - mx[hh]);"),
+    "lse_without_max": ("out_lse[hh * lse_stride] = mx[hh] + log(sum[hh]);",
+                        "out_lse[hh * lse_stride] = log(sum[hh]);"),
     "value_rows_from_keys": ("const uint16_t* v_row = v + ", "const uint16_t* v_row = k + "),
-    "query_head_of_group_leader": ("q + (pos * Hq + h) * D", "q + (pos * Hq + g * G) * D"),
-    "attends_across_sequences": [("cu_seqlens[s], pos, scores", "0, pos, scores"),
-                                 ("double* scores = (double*)malloc(sizeof(double) * (size_t)(longest > 0 ? longest : 1));",
-                                  "double* scores = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));")],
-    "no_max_shift": ("l += exp(scores[t] - m);", "l += exp(scores[t]);"),
-    "float32_dot": ("double dot = 0.0;", "float dot = 0.0f;"),
+    "query_head_of_group_leader": ("qt[d * G + hh] = bf16_bits_to_double(q_rows[hh * D + d]);",
+                                   "qt[d * G + hh] = bf16_bits_to_double(q_rows[d]);"),
+    "attends_across_sequences": [("scale, cu_seqlens[s], pos,", "scale, 0, pos,"),
+                                 ("(size_t)(G * (longest > 0 ? longest : 1) + 3 * G + G * D + D));",
+                                  "(size_t)(G * (T > 0 ? T : 1) + 3 * G + G * D + D));")],
+    "no_max_shift": ("l += exp(x[t] - m);", "l += exp(x[t]);"),
+    "float32_dot": ("dot[hh] += qt[d * G + hh] * kd;",
+                    "dot[hh] = (float)(dot[hh] + qt[d * G + hh] * kd);"),
     "keyrange_end_inclusive": ("(key_end - 1 < pos) ? key_end - 1 : pos",
                                "(key_end < pos) ? key_end : pos"),
     "keyrange_begin_ignored": ("const int64_t first = key_begin > 0 ? key_begin : 0;",
                                "const int64_t first = 0;"),
-    "keyrange_empty_lse_zero": ("lse_out[h * ntok + ti] = -INFINITY;",
-                                "lse_out[h * ntok + ti] = 0.0;"),
-    "bidirectional_masked": ("scale, 0, S - 1, scores,", "scale, 0, pos, scores,"),
-    "bidirectional_misses_last_key": ("scale, 0, S - 1, scores,", "scale, 0, S - 2 + (S == 1), scores,"),
+    "keyrange_empty_lse_zero": ("lse_out[(h0 + hh) * ntok + ti] = -INFINITY;",
+                                "lse_out[(h0 + hh) * ntok + ti] = 0.0;"),
+    "bidirectional_masked": ("scale, 0, S - 1,", "scale, 0, pos,"),
+    "bidirectional_misses_last_key": ("scale, 0, S - 1,", "scale, 0, S - 2 + (S == 1),"),
     "rope_sin_sign": ("o[i + half] = hi * c + lo * sn;", "o[i + half] = hi * c - lo * sn;"),
     "rope_frequency_exponent": ("pow(theta, -2.0 * (double)i / (double)D)",
                                 "pow(theta, -1.0 * (double)i / (double)D)"),
