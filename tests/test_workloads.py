@@ -80,3 +80,13 @@ def test_sample_tokens_cover_edges():
     for must in (0, 8183, 8184, 8184 + 8198, 63, 64):
         assert must in t
     assert t.max() < 8184 + 8199
+
+
+def test_block_tokens_one_per_query_block_with_moving_offset():
+    t = workloads.block_tokens([70, 5, 64])
+    assert t.tolist() == [0, 33, 66, 70, 75, 108]
+    # the S=10231 workload: 320 blocks of 32 tokens, offsets 0, 1, .., 31, 0, 1, ..
+    t = workloads.block_tokens([10231])
+    assert len(t) == 320
+    assert all(int(x) // 32 == b and int(x) % 32 == b % 32 for b, x in enumerate(t[:-1]))
+    assert int(t[-1]) == 10230

@@ -216,6 +216,19 @@ def generate(w: Workload) -> dict:
     return out
 
 
+def block_tokens(seqlens, block: int = 32) -> np.ndarray:
+    """One packed query position per ``block``-token query block of every sequence, its
+    offset in the block moving with the block index: local position block*b + (b mod block),
+    clamped to the sequence's last token."""
+    picks = []
+    start = 0
+    for s in seqlens:
+        for b in range((s + block - 1) // block):
+            picks.append(start + min(block * b + b % block, s - 1))
+        start += s
+    return np.unique(np.asarray(picks, dtype=np.int64))
+
+
 def sample_tokens(seqlens, n_random: int, seed: int, tile: int = 64) -> np.ndarray:
     """Packed query positions to check at full size.
 
