@@ -23,7 +23,9 @@ import os
 import threading
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIBRARY = os.path.join(PKG_DIR, "libh3attn.so")
+# The in-tree build; H3ATTN_LIBRARY names another build of the same sources (the host-side
+# sanitizer test build, for instance).
+LIBRARY = os.environ.get("H3ATTN_LIBRARY") or os.path.join(PKG_DIR, "libh3attn.so")
 
 # status codes (include/h3attn.h)
 (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_SCALE, ERR_LAUNCH, ERR_DEVICE,
@@ -36,7 +38,7 @@ PROLOGUE_ROPE = 1                # flag of h3attn_qk_norm_rope
 EXPORTED = ("h3attn_gqa_causal_fwd", "h3attn_gqa_fwd", "h3attn_gqa_causal_varlen_fwd",
             "h3attn_gqa_causal_splitkv_fwd", "h3attn_gqa_causal_splitkv_workspace_bytes",
             "h3attn_qk_norm_rope", "h3attn_gqa_causal_qnorm_rope_fwd", "h3attn_pool_tokens",
-            "h3attn_pool_tokens_out_len",
+            "h3attn_pool_tokens_out_len", "h3attn_check_cu_seqlens",
             "h3attn_status_string", "h3attn_version",
             "h3attn_lds_bytes")
 
@@ -98,6 +100,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         lib.h3attn_version.restype = i32
         lib.h3attn_lds_bytes.argtypes = [i32, i32]
         lib.h3attn_lds_bytes.restype = i32
+        lib.h3attn_check_cu_seqlens.argtypes = [vp, i32, i32, i32]
+        lib.h3attn_check_cu_seqlens.restype = i32
         if path == LIBRARY:
             _lib = lib
         return lib
@@ -298,6 +302,17 @@ def gqa_causal_qnorm_rope_fwd(q, k, v, q_norm_weight=None, eps: float = 1e-6, ro
         PROLOGUE_ROPE if rope else 0, _stream_handle(stream, q.device))
     _check(rc)
     return out, lse
+
+
+def check_cu_seqlens(cu_seqlens, total_tokens: int, max_seqlen: int) -> int:
+    """Status of the library's host-side check of packed-batch offsets (a host int32
+    sequence of num_seqs + 1 values); OK when they are valid for total_tokens / max_seqlen."""
+    import numpy as np
+
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    ptr = cu.ctypes.data if cu.size else None
+    return int(load_library().h3attn_check_cu_seqlens(ptr, int(cu.size) - 1, int(total_tokens),
+                                                      int(max_seqlen)))
 
 
 def pool_tokens_out_len(T: int, begin: int, end: int, factor: int) -> int:

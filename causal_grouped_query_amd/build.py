@@ -64,5 +64,37 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     return LIBRARY
 
 
+# Host-side sanitizers for a CPU-only test build: each -fsanitize= applies to the host
+# pass only (the device code is compiled as usual and never run by that test).
+SANITIZE_HOST_FLAGS = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-shared-libsan",
+]
+
+
+def build_host_sanitized(output: str) -> str:
+    """Build the library with AddressSanitizer and UndefinedBehaviorSanitizer on its host
+    code into ``output`` (not the in-tree library).  It needs the sanitizer runtime
+    (``sanitizer_runtime()``) preloaded into the process that loads it."""
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + ["-O1"] + SANITIZE_HOST_FLAGS
+    cmd = [hipcc(), *flags, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
+           *SOURCES, "-o", output]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + (res.stdout + res.stderr)[-4000:])
+    return output
+
+
+def sanitizer_runtime() -> str | None:
+    """Path of the shared AddressSanitizer runtime that matches hipcc's clang, if present."""
+    import glob
+
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

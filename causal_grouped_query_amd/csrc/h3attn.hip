@@ -12,7 +12,9 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "gqa_fwd_kernel.hpp"
 #include "gqa_fwd_wide_kernel.hpp"
@@ -211,6 +213,27 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace
 
+namespace {
+
+bool check_cu_seqlens_requested() {
+  const char* e = std::getenv("H3ATTN_CHECK_CU_SEQLENS");
+  return e != nullptr && std::strcmp(e, "1") == 0;
+}
+
+// The debug check of the varlen call: copy the device offsets to the host, in order on the
+// caller's stream (after whatever wrote them), wait for the copy, and validate.
+int debug_check_cu_seqlens(const int32_t* cu_dev, int num_seqs, int total_tokens,
+                           int max_seqlen, hipStream_t stream) {
+  std::vector<int32_t> host((size_t)num_seqs + 1);
+  if (hipMemcpyAsync(host.data(), cu_dev, host.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                     stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return H3ATTN_ERR_LAUNCH;
+  return h3attn_check_cu_seqlens(host.data(), num_seqs, total_tokens, max_seqlen);
+}
+
+}  // namespace
+
 extern "C" {
 
 int h3attn_gqa_causal_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -235,6 +258,18 @@ int h3attn_gqa_causal_fwd(const void* q, const void* k, const void* v, void* o, 
   return dispatch<false>(D, Hq / Hkv, p, static_cast<hipStream_t>(hip_stream));
 }
 
+int h3attn_check_cu_seqlens(const int32_t* cu, int num_seqs, int total_tokens, int max_seqlen) {
+  if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0) return H3ATTN_ERR_SHAPE;
+  if (num_seqs > 0 && !cu) return H3ATTN_ERR_NULL;
+  if (num_seqs == 0) return total_tokens == 0 ? H3ATTN_OK : H3ATTN_ERR_SHAPE;
+  if (cu[0] != 0 || cu[num_seqs] != total_tokens) return H3ATTN_ERR_SHAPE;
+  for (int s = 0; s < num_seqs; ++s) {
+    const long long len = (long long)cu[s + 1] - cu[s];
+    if (len < 0 || len > max_seqlen) return H3ATTN_ERR_SHAPE;
+  }
+  return H3ATTN_OK;
+}
+
 int h3attn_gqa_causal_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                  const int32_t* cu_seqlens, int num_seqs, int total_tokens,
                                  int max_seqlen, int Hq, int Hkv, int D, float softmax_scale,
@@ -247,6 +282,11 @@ int h3attn_gqa_causal_varlen_fwd(const void* q, const void* k, const void* v, vo
   if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return H3ATTN_ERR_ALIGN;
   if (total_tokens == 0 || max_seqlen == 0) return H3ATTN_OK;
   if (!device_ok()) return H3ATTN_ERR_DEVICE;
+  if (check_cu_seqlens_requested()) {
+    const int crc = debug_check_cu_seqlens(cu_seqlens, num_seqs, total_tokens, max_seqlen,
+                                           static_cast<hipStream_t>(hip_stream));
+    if (crc != H3ATTN_OK) return crc;
+  }
   FwdParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);

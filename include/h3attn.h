@@ -107,7 +107,10 @@ H3ATTN_API int h3attn_gqa_fwd(const void* q, const void* k, const void* v, void*
 /*
  * Packed variable-length causal GQA forward: num_seqs independent sequences
  * concatenated along the token axis.  Positions are local to each sequence and
- * no query attends to another sequence's keys.
+ * no query attends to another sequence's keys.  The issue's table of runs
+ * (section "Systematic single-variable experiments") lists the failing encoder
+ * lengths 8184, 8199, 8510 and 10231 tokens; one call with those four sequences
+ * packed (35124 tokens) serves them all.
  *
  *   q    [T, Hq,  D] bf16   k, v [T, Hkv, D] bf16   o [T, Hq, D] bf16
  *   lse  [Hq, T] fp32, indexed by packed token (may be NULL)
@@ -118,14 +121,32 @@ H3ATTN_API int h3attn_gqa_fwd(const void* q, const void* k, const void* v, void*
  *
  * The offsets live on the device and are not read on the host.  The kernel
  * clamps each sequence to [0, T] and to max_seqlen, so invalid offsets give
- * unspecified (but in-bounds) results, never an out-of-bounds access.
- * total_tokens == 0 is a no-op (tensor pointers may then be NULL); so is
- * max_seqlen == 0.
+ * unspecified (but in-bounds) results, never an out-of-bounds access; in
+ * particular the rows of a sequence longer than max_seqlen past its first
+ * max_seqlen tokens are not written.  total_tokens == 0 is a no-op (tensor
+ * pointers may then be NULL); so is max_seqlen == 0.
+ *
+ * Debug check: with the environment variable H3ATTN_CHECK_CU_SEQLENS set to 1
+ * when the call is made, the call first copies cu_seqlens to the host (on
+ * hip_stream, waiting for the copy to finish) and validates it with
+ * h3attn_check_cu_seqlens; an offset table that fails the check returns
+ * H3ATTN_ERR_SHAPE and launches nothing, a failed copy H3ATTN_ERR_LAUNCH.
  */
 H3ATTN_API int h3attn_gqa_causal_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                  const int32_t* cu_seqlens, int num_seqs, int total_tokens,
                                  int max_seqlen, int Hq, int Hkv, int D, float softmax_scale,
                                  void* hip_stream);
+
+/*
+ * Host-side validation of a packed batch's offsets (no GPU work): cu_seqlens_host
+ * is a HOST int32[num_seqs + 1].  Returns H3ATTN_OK when cu[0] = 0, the offsets
+ * do not decrease, cu[num_seqs] = total_tokens and every length cu[s+1] - cu[s]
+ * is at most max_seqlen; H3ATTN_ERR_NULL for a NULL table with num_seqs > 0;
+ * H3ATTN_ERR_SHAPE otherwise (also for negative counts).  This is the check the
+ * varlen forward runs under H3ATTN_CHECK_CU_SEQLENS=1.
+ */
+H3ATTN_API int h3attn_check_cu_seqlens(const int32_t* cu_seqlens_host, int num_seqs,
+                                       int total_tokens, int max_seqlen);
 
 /*
  * Split-KV (multi-dispatch) causal GQA forward over one sequence: the first fix

@@ -188,6 +188,34 @@ def test_varlen_equals_single_calls(lib, Hq, Hkv, D, seed):
     assert_close(to_f64(o), lf, o_ref, lse_ref, f"varlen mixed lengths {Hq}/{Hkv} D={D}")
 
 
+def test_varlen_offsets_check_under_env_switch(lib, monkeypatch):
+    """With H3ATTN_CHECK_CU_SEQLENS=1 the packed call reads the offsets back and refuses a
+    max_seqlen below the longest sequence (and a malformed table) before launching; with
+    valid arguments it gives the same bits as the unchecked call."""
+    import torch
+
+    lens = [40, 130, 7]
+    T = sum(lens)
+    q, k, v = normal_inputs(150, T, 16, 2, 128)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
+    monkeypatch.setenv("H3ATTN_CHECK_CU_SEQLENS", "1")
+    sentinel = torch.full((T, 16, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    o = sentinel.clone()
+    for bad_cu, max_seqlen in ((cu, 129), (cu, 1), (torch.tensor([0, 40, 30, T], dtype=torch.int32,
+                                                                  device="cuda"), 130)):
+        with pytest.raises(lib.H3AttnError) as err:
+            lib.gqa_causal_varlen_fwd(qd, kd, vd, bad_cu, max_seqlen, out=o)
+        assert err.value.status == lib.ERR_SHAPE
+        torch.cuda.synchronize()
+        assert torch.equal(o, sentinel), "a refused call wrote its output"
+    o1, l1 = lib.gqa_causal_varlen_fwd(qd, kd, vd, cu, 130)
+    monkeypatch.delenv("H3ATTN_CHECK_CU_SEQLENS")
+    o2, l2 = lib.gqa_causal_varlen_fwd(qd, kd, vd, cu, 130)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_deterministic_and_lse_optional(lib):
     import torch
 
