@@ -31,6 +31,7 @@ LIBRARY = os.environ.get("H3ATTN_LIBRARY") or os.path.join(PKG_DIR, "libh3attn.s
 (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_SCALE, ERR_LAUNCH, ERR_DEVICE,
  ERR_WORKSPACE) = range(9)
 MAX_SPLITS = 64
+NOALLOC_SCRATCH_BYTES = 64 << 20   # fixed scratch of h3attn_gqa_causal_splitkv_fwd_noalloc
 
 NONCAUSAL, O_HEAD_MAJOR = 1, 2   # flags of h3attn_gqa_fwd
 PROLOGUE_ROPE = 1                # flag of h3attn_qk_norm_rope
@@ -39,6 +40,7 @@ EXPORTED = ("h3attn_gqa_causal_fwd", "h3attn_gqa_fwd", "h3attn_gqa_causal_varlen
             "h3attn_gqa_causal_splitkv_fwd", "h3attn_gqa_causal_splitkv_workspace_bytes",
             "h3attn_qk_norm_rope", "h3attn_gqa_causal_qnorm_rope_fwd", "h3attn_pool_tokens",
             "h3attn_pool_tokens_out_len", "h3attn_check_cu_seqlens",
+            "h3attn_gqa_causal_splitkv_fwd_noalloc",
             "h3attn_status_string", "h3attn_version",
             "h3attn_lds_bytes")
 
@@ -100,6 +102,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         lib.h3attn_version.restype = i32
         lib.h3attn_lds_bytes.argtypes = [i32, i32]
         lib.h3attn_lds_bytes.restype = i32
+        lib.h3attn_gqa_causal_splitkv_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32,
+                                                              i32, f32, i32, vp]
+        lib.h3attn_gqa_causal_splitkv_fwd_noalloc.restype = i32
         lib.h3attn_check_cu_seqlens.argtypes = [vp, i32, i32, i32]
         lib.h3attn_check_cu_seqlens.restype = i32
         if path == LIBRARY:
@@ -414,7 +419,27 @@ def gqa_causal_splitkv_fwd(q, k, v, num_splits: int, softmax_scale: float | None
     return out, lse
 
 
+def gqa_causal_splitkv_fwd_noalloc(q, k, v, num_splits: int, softmax_scale: float | None = None,
+                                   out=None, lse=None, return_lse: bool = True, stream=None):
+    """:func:`gqa_causal_splitkv_fwd` with the library's fixed scratch array as its workspace
+    (for callers that cannot allocate device memory: pass ``out`` and ``lse``).  The
+    workspace need must not exceed :data:`NOALLOC_SCRATCH_BYTES`; calls that overlap on
+    one GPU race on the shared array."""
+    _check_tensors(q, k, v)
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    out, lse = _outputs(q, out, lse, return_lse)
+    rc = load_library().h3attn_gqa_causal_splitkv_fwd_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, S, Hq, Hkv, D, scale, int(num_splits),
+        _stream_handle(stream, q.device))
+    _check(rc)
+    return out, lse
+
+
 __all__ = ["gqa_causal_fwd", "gqa_fwd", "gqa_causal_varlen_fwd", "gqa_causal_splitkv_fwd",
+           "gqa_causal_splitkv_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
            "splitkv_workspace_bytes", "status_string", "version", "lds_bytes", "load_library",
            "H3AttnError", "LIBRARY", "EXPORTED", "MAX_SPLITS", "NONCAUSAL", "O_HEAD_MAJOR",
            "qk_norm_rope", "gqa_causal_qnorm_rope_fwd", "PROLOGUE_ROPE", "pool_tokens",

@@ -14,6 +14,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "gqa_fwd_kernel.hpp"
@@ -50,6 +51,31 @@ bool device_ok() {
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Workspace of h3attn_gqa_causal_splitkv_fwd_noalloc: a fixed array in the code object, one
+// copy per GPU the library runs on, held until the process ends.  Host code never uses the
+// array's name as an address: each device's copy is looked up once (hipGetSymbolAddress,
+// with that device current) and the pointer kept per device.
+static_assert(H3ATTN_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[H3ATTN_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mutex;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of the scratch array, or nullptr if the lookup fails.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (ptr == nullptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return nullptr;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
 
 template <int D, int G, bool VARLEN, bool CAUSAL>
 int launch(FwdParams p, hipStream_t stream) {
@@ -480,6 +506,23 @@ int h3attn_gqa_causal_splitkv_fwd(const void* q, const void* k, const void* v, v
   return dispatch_split(D, Hq / Hkv, p, static_cast<hipStream_t>(hip_stream));
 }
 
+int h3attn_gqa_causal_splitkv_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                                          float* lse, int S, int Hq, int Hkv, int D,
+                                          float softmax_scale, int num_splits, void* hip_stream) {
+  const int rc = check_common(q, k, v, o, lse, S, Hq, Hkv, D, softmax_scale);
+  if (rc != H3ATTN_OK) return rc;
+  if (num_splits < 1 || num_splits > H3ATTN_MAX_SPLITS) return H3ATTN_ERR_SHAPE;
+  if (S == 0) return H3ATTN_OK;
+  size_t lse_off = 0;
+  if (split_workspace_layout(S, Hq, D, num_splits, &lse_off) > H3ATTN_NOALLOC_SCRATCH_BYTES)
+    return H3ATTN_ERR_WORKSPACE;
+  if (!device_ok()) return H3ATTN_ERR_DEVICE;
+  void* ws = device_scratch();
+  if (ws == nullptr) return H3ATTN_ERR_DEVICE;
+  return h3attn_gqa_causal_splitkv_fwd(q, k, v, o, lse, S, Hq, Hkv, D, softmax_scale, num_splits,
+                                       ws, H3ATTN_NOALLOC_SCRATCH_BYTES, hip_stream);
+}
+
 const char* h3attn_status_string(int status) {
   switch (status) {
     case H3ATTN_OK: return "ok";
@@ -498,7 +541,8 @@ const char* h3attn_status_string(int status) {
     case H3ATTN_ERR_DEVICE: return "no usable gfx950 device is current";
     case H3ATTN_ERR_WORKSPACE:
       return "workspace is NULL, not 256-byte aligned, or smaller than "
-             "h3attn_gqa_causal_splitkv_workspace_bytes()";
+             "h3attn_gqa_causal_splitkv_workspace_bytes() (the allocation-free call: that "
+             "size exceeds its fixed scratch, H3ATTN_NOALLOC_SCRATCH_BYTES = 64 MiB)";
     default: return "unknown status";
   }
 }

@@ -179,6 +179,33 @@ H3ATTN_API int h3attn_gqa_causal_splitkv_fwd(const void* q, const void* k, const
                                              void* workspace, size_t workspace_bytes,
                                              void* hip_stream);
 
+/* Size of the fixed device scratch array h3attn_gqa_causal_splitkv_fwd_noalloc uses
+ * (64 MiB, one copy per GPU the library runs on, held until the process ends). */
+#define H3ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): h3attn_gqa_causal_splitkv_fwd with
+ * the workspace taken from a fixed array inside the library instead of from the
+ * caller.  Same arguments, checks and results as h3attn_gqa_causal_splitkv_fwd,
+ * without workspace / workspace_bytes.
+ *
+ * The call allocates nothing (no hipMalloc, no allocating library routine).  Its
+ * first call on a device looks up that device's copy of the array once.  A call whose
+ * workspace need, h3attn_gqa_causal_splitkv_workspace_bytes(S, Hq, D, num_splits),
+ * exceeds H3ATTN_NOALLOC_SCRATCH_BYTES returns H3ATTN_ERR_WORKSPACE and launches
+ * nothing; H3ATTN_ERR_DEVICE if the array cannot be looked up.  Every call on one GPU
+ * uses the same array: calls that overlap on one GPU (different streams, or different
+ * host threads) race on it and give undefined results; calls in order on one stream
+ * are safe.  The array keeps whatever the last call left; no call relies on its
+ * contents.
+ */
+H3ATTN_API int h3attn_gqa_causal_splitkv_fwd_noalloc(const void* q, const void* k,
+                                                     const void* v, void* o, float* lse,
+                                                     int S, int Hq, int Hkv, int D,
+                                                     float softmax_scale, int num_splits,
+                                                     void* hip_stream);
+
 /* Workspace bytes h3attn_gqa_causal_splitkv_fwd needs: partial O, fp32
  * [num_splits, S, Hq, D], then partial LSE, fp32 [num_splits, Hq, S], at the next
  * 256-byte boundary.  0 for invalid arguments. */
