@@ -135,7 +135,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
       const uint16_t* qp = p.q + ((size_t)(start + my_tok[r]) * p.hq + my_head) * D + 8 * half;
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds)
-        qf[r][ds] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 16 * ds));
+        qf[r][ds] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(qp + 16 * ds)));
     } else {
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) qf[r][ds] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
@@ -395,14 +395,19 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
                  "+{v[252:255]}"(fx[6])
                :
                : "memory");
+  // O goes out through LDS so that every store instruction writes whole 256-byte rows.  The
+  // K half of the ring (64 KB, no longer read once every wave has passed this barrier) holds
+  // a [256 rows][128] bf16 stage, wave w owning rows 64w .. 64w+63; the 16-byte chunk c of
+  // row r sits at chunk c ^ (r & 15), so both the row-wise writes and the chunk-wise reads
+  // below spread over all LDS banks.
+  __syncthreads();
+  uint8_t* const ostage = reinterpret_cast<uint8_t*>(&k_lds[0][0]) + wave * 64 * 256;
+  float l_tot[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const float l_tot = pair_sum(l_run[r]);
-    if (!my_valid[r]) continue;
-    const float inv = 1.0f / l_tot;
-    uint16_t* op = p.o + (p.o_head_major
-                              ? ((size_t)my_head * p.total_tokens + start + my_tok[r]) * D
-                              : ((size_t)(start + my_tok[r]) * p.hq + my_head) * D);
+    l_tot[r] = pair_sum(l_run[r]);
+    const float inv = 1.0f / l_tot[r];
+    const int row = 32 * r + col;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const f32x16 ov = o_read(acc[r][db]);
@@ -412,12 +417,34 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = ov[4 * r4 + e] * inv;
         const bf16x4 y = __builtin_convertvector(x, bf16x4);
-        *(u32x2*)(op + 32 * db + 8 * r4 + 4 * half) = __builtin_bit_cast(u32x2, y);
+        const int chunk = (4 * db + r4) ^ (row & 15);    // d = 32 db + 8 r4 + 4 half + e
+        *(u32x2*)(ostage + row * 256 + chunk * 16 + 8 * half) = __builtin_bit_cast(u32x2, y);
       }
     }
-    if (p.lse != nullptr && half == 0)
+  }
+  // each lane stores 16 bytes (8 elements, chunk c) of one row; 4 rows per instruction.
+  // Non-temporal: O is written once and not read again here.
+  {
+    const int c = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 4 * i + (lane >> 4);
+      const u32x4 val = *(const u32x4*)(ostage + row * 256 + ((c ^ (row & 15)) * 16));
+      const int rcol = row & 31;
+      const int tok = wq0 + (row >> 5) * C::TOK_RB + rcol / G;
+      if (tok < len) {
+        const int head = g * G + rcol % G;
+        uint16_t* op = p.o + (p.o_head_major ? ((size_t)head * p.total_tokens + start + tok) * D
+                                             : ((size_t)(start + tok) * p.hq + head) * D);
+        __builtin_nontemporal_store(val, (u32x4*)(op + 8 * c));
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (p.lse != nullptr && half == 0 && my_valid[r])
       p.lse[(size_t)my_head * p.total_tokens + start + my_tok[r]] =
-          (m_run[r] + __builtin_amdgcn_logf(l_tot)) * LN2;
+          (m_run[r] + __builtin_amdgcn_logf(l_tot[r])) * LN2;
   }
 }
 
