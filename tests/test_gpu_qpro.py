@@ -72,6 +72,9 @@ CASES = [  # S, Hq, Hkv, D, seed, norm, rope, explicit positions
     (333, 8, 2, 64, 707, True, True, True),      # D = 64, G = 4
     (260, 16, 2, 64, 708, True, True, False),    # D = 64, G = 8
     (150, 16, 2, 128, 709, True, True, "far"),   # positions near 10^5 (fp64 angle reduction)
+    (517, 4, 4, 64, 710, True, True, False),     # D = 64, G = 1, several blocks, ragged
+    (190, 8, 4, 64, 711, True, True, True),      # D = 64, G = 2
+    (270, 8, 4, 128, 712, True, True, False),    # D = 128, G = 2, norm + RoPE
 ]
 
 
