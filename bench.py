@@ -38,10 +38,12 @@ def log(msg: str) -> None:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # about 2.2 s timed after 0.45 s of warmup at S=10231: the shader clock and power
-    # readings are refreshed by the firmware about once a second
-    ap.add_argument("--steps", type=int, default=1500)
-    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-seconds", type=float, default=1.2,
+                    help="untimed launches of the same step, for at least this long, before "
+                         "the warmup steps: the board ramps its clock over the first tens of ms "
+                         "of load, and the clock readings refresh about once a second")
     ap.add_argument("--workload", default=workloads.PRIMARY,
                     choices=sorted(workloads.ALL_WORKLOADS))
     ap.add_argument("--path", default="fused",
@@ -132,7 +134,7 @@ class ClockSampler:
         self.error = None
         self.thread = None
         self.stop_flag = False
-        self.begin = self.end = None
+        self.begin = self.end = self.window_begin = None
         try:
             import amdsmi
 
@@ -185,14 +187,16 @@ class ClockSampler:
                 pass
 
     def refreshes(self):
-        """The table refreshes first seen inside the timed region, one sample each."""
-        if self.begin is None:
+        """The table refreshes first seen inside [window_begin, end], one sample each
+        (window_begin defaults to the start of the timed region)."""
+        lo = self.window_begin if self.window_begin is not None else self.begin
+        if lo is None or self.end is None:
             return []
-        before = [smp[1] for smp in self.samples if smp[0] < self.begin]
+        before = [smp[1] for smp in self.samples if smp[0] < lo]
         seen = {before[-1]} if before else set()
         out = []
         for smp in self.samples:
-            if self.begin <= smp[0] <= self.end and smp[1] not in seen and smp[2] is not None:
+            if lo <= smp[0] <= self.end and smp[1] not in seen and smp[2] is not None:
                 seen.add(smp[1])
                 out.append(smp)
         return out
@@ -202,10 +206,11 @@ class ClockSampler:
         if not fresh:
             return {"source": "amdsmi gpu_metrics", "mhz_mean": None,
                     "error": self.error or "the metrics table was not refreshed inside the "
-                                           "timed region (run more steps)"}
+                                           "sampled window"}
         c = np.array([smp[2] for smp in fresh])
         out = {"source": "amdsmi gpu_metrics current_gfxclks (mean over the 8 XCDs), each "
-                         "firmware refresh (about 1/s) published inside the timed region",
+                         "firmware refresh (about 1/s) published from 0.25 s into the settle "
+                         "launches to the end of the timed launches",
                "refreshes": int(len(c)), "mhz_mean": round(float(c.mean()), 1),
                "xcd_mhz_last": fresh[-1][3]}
         pw = [smp[4] for smp in fresh if smp[4] is not None]
@@ -544,10 +549,18 @@ def main():
 
     sampler = ClockSampler()
     sampler.start()
+    settle_steps, t_settle = 0, time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_seconds:
+        for _ in range(20):
+            step()
+        settle_steps += 20
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_settle
+    sampler.window_begin = t_settle + min(0.25, settle_s)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup} done")
+    log(f"settle {settle_steps} launches in {settle_s:.2f} s, warmup {args.warmup} done")
 
     # timed region: K steps; events on the launch stream around each launch
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -598,6 +611,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"launches": settle_steps, "seconds": round(settle_s, 3),
+                   "note": "untimed launches of the same step before the warmup, so the timed "
+                           "launches run at the board's steady clock"},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

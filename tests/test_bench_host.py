@@ -96,7 +96,7 @@ def test_clock_sampler_never_raises_without_a_gpu():
 
 def test_clock_sampler_keeps_each_refresh_inside_the_timed_region_once():
     s = bench.ClockSampler.__new__(bench.ClockSampler)
-    s.error, s.period = None, 0.005
+    s.error, s.period, s.window_begin = None, 0.005, None
     # (time, table counter, mean clock, XCD clocks, power): the table refreshes at t=0.5
     # (before the timed region), t=1.5 and t=2.5; the region is [1.0, 3.0]
     s.samples = [(0.1, 10, 400.0, [400] * 8, 250), (0.6, 11, 1900.0, [1900] * 8, 1300),
@@ -109,6 +109,8 @@ def test_clock_sampler_keeps_each_refresh_inside_the_timed_region_once():
     assert out["mhz_mean"] == 1900.0 and out["socket_power_w_mean"] == 1355.0
     s.begin, s.end = 1.0, 1.4           # no refresh inside: nothing is reported
     assert s.summary()["mhz_mean"] is None
+    s.window_begin = 0.3                # a window opened before the timed region
+    assert s.summary()["refreshes"] == 1 and s.summary()["mhz_mean"] == 1900.0
 
 
 def test_default_workload_is_the_metric_workload():
