@@ -6,7 +6,7 @@ query token and head of O (relative L2 and max |error| over the whole tensor) an
 The larger workloads (the packed T=35124 batch, the S=32768 stress workload and the two
 DiT sizes) are compared on one query token of every 32-token query block, its offset in
 the block moving with the block index (position 32 b + (b mod 32)), every head; the
-oracle on all of their rows would take hours on the host.
+oracle on all of their rows takes minutes each on the host, too long for a GPU test run.
 """
 
 from __future__ import annotations
