@@ -68,6 +68,12 @@ struct WideConfig {
   static_assert(TILE_PIECES % NW == 0, "tile fill divides over waves");
 };
 
+// log2 units added to a row's running max when the max path raises it.  After a raise the
+// row's largest weight is 2^-16, and the next raise needs a key scoring about 28 log2 units
+// higher (16 of headroom, 12 for one weight to push a lane's 16-weight sum past the limit),
+// so rows whose max keeps growing (large-logit inputs) take the max path far less often.
+constexpr float MAX_HEADROOM = 16.0f;
+
 template <class C, bool VARLEN, bool CAUSAL>
 __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p) {
   using namespace wide::d128;
@@ -249,7 +255,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[r][e]);
       mx = pair_max(mx);
       const bool raise = (((flagged >> col) | (flagged >> (col + 32))) & 1) != 0;
-      const float m_new = raise ? fmaxf(m_run[r], mx * c) : m_run[r];
+      // a raised max sits MAX_HEADROOM above the sub-tile's max
+      const float m_new = raise ? fmaxf(m_run[r], mx * c + MAX_HEADROOM) : m_run[r];
       const float alpha = __builtin_amdgcn_exp2f(m_run[r] - m_new);
       l_run[r] *= alpha;
       if (r == 0)
