@@ -187,6 +187,32 @@ def phase_lines(D, do_scores, do_pv, do_softmax, fills=0, desc=False):
     return units, lines
 
 
+MIN_REUSE_GAP = 2   # MFMAs between an MFMA reading a fragment buffer and an LDS read into it
+
+
+def check_fragment_reuse(lines):
+    """An LDS read may refill a fragment buffer only after MIN_REUSE_GAP further MFMAs have
+    issued past the last MFMA that reads it: the read's data can land before a queued MFMA
+    has fetched its operand (seen with one MFMA in between: wrong results).  ``lines`` is a
+    phase followed by the next phase, so the reuse across the phase boundary is checked
+    too (the code between two phases only adds distance)."""
+    last_reader = {}      # buffer base register -> MFMA count at its last read
+    n_mfma = 0
+    for ln in lines:
+        if ln.startswith("v_mfma"):
+            n_mfma += 1
+            a_op = ln.split(",")[1].strip()
+            if a_op.startswith("v["):
+                last_reader[int(a_op[2:].split(":")[0])] = n_mfma
+        elif ln.startswith("ds_read"):
+            dst = ln.split()[1].rstrip(",")
+            base = int(dst[2:].split(":")[0])
+            for b in (base, base - 2):           # a transposing read fills half a buffer
+                if b in last_reader:
+                    gap = n_mfma - last_reader[b]
+                    assert gap >= MIN_REUSE_GAP, (ln, gap)
+
+
 def emit(D, name, do_scores, do_pv, do_softmax, fills=0, fill_only=False, skippable=False,
          desc=False):
     nds, ndb = D // 16, D // 32
@@ -313,6 +339,10 @@ def header():
         for name, s, p, x in VARIANTS:
             out.append(emit(D, "phase_" + name, s, p, x))
             out.append("")
+        _, up = phase_lines(D, True, True, True, FILLS_PER_PHASE, False)
+        _, down = phase_lines(D, True, True, True, FILLS_PER_PHASE, True)
+        check_fragment_reuse(up + down)
+        check_fragment_reuse(down + up)
         out.append(emit(D, "phase_step_up", True, True, True, fills=FILLS_PER_PHASE, skippable=True))
         out.append("")
         out.append(emit(D, "phase_step_down", True, True, True, fills=FILLS_PER_PHASE,
