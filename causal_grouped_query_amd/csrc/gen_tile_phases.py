@@ -213,17 +213,9 @@ def check_fragment_reuse(lines):
                     assert gap >= MIN_REUSE_GAP, (ln, gap)
 
 
-def emit(D, name, do_scores, do_pv, do_softmax, fills=0, fill_only=False, skippable=False,
-         desc=False):
+def emit(D, name, do_scores, do_pv, do_softmax, fills=0, skippable=False, desc=False):
     nds, ndb = D // 16, D // 32
     units, lines = phase_lines(D, do_scores, do_pv, do_softmax, fills, desc)
-    if fill_only:
-        # same operands as the full phase with fills; only the fill loads are issued (the
-        # outputs are left undefined: the caller has no sub-tile of its own here)
-        units = []
-        lines = []
-        for i in range(fills):
-            lines += fill_piece(i, fills, desc)
     if skippable:
         # a wave-uniform test skips the computation; the fill loads are issued either way
         fl = []
@@ -322,9 +314,9 @@ def emit_o_helpers(D):
     return "\n\n".join(out)
 
 
-VARIANTS = (("full", True, True, True), ("pv_softmax", False, True, True),
-            ("scores_softmax", True, False, True), ("softmax", False, False, True),
-            ("pv", False, True, False), ("scores", True, False, False))
+# the prologue's phases (the loop uses phase_step_up / phase_step_down): scores of sub-tile 0,
+# then scores of sub-tile 1 with the softmax of sub-tile 0
+VARIANTS = (("scores_softmax", True, False, True), ("scores", True, False, False))
 
 
 def header():
