@@ -18,17 +18,27 @@ The MFMAs are v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  Layouts are those o
 kernel: S^T tiles hold 16 keys of one query row per lane, which is the B-operand layout of
 the P.V MFMA, so P needs no data movement.
 
-Register use: fragments and softmax temporaries live in fixed registers v[228:255] that the
-asm statements declare clobbered (inline asm cannot name part of an operand, and the V^T
-fragment is two 8-byte transposing reads into one 16-byte operand).  Everything that lives
-across phases is a compiler operand; O and Q (MFMA operands only) are held in AGPRs.
+The loop's phases (phase_step_up / phase_step_down) also issue this wave's quarter of one
+K or V tile (4 x 1 KB LDS-DMA loads between the MFMAs), and begin with a scalar compare of
+the sub-tile index against the wave's last one: past it the block branches to the loads
+alone.  The two variants differ only in the order of the loads' 16-row steps (up, then back
+down), so one VGPR holds the lane's load offset for every piece.
+
+Register use: fragments and softmax temporaries live in fixed registers v[228:255] (inline
+asm cannot name part of an operand, and the V^T fragment is two 8-byte transposing reads
+into one 16-byte operand); every block takes them as read-write operands pinned to those
+registers, and the kernel keeps them live from before the first block to after the last,
+so the compiler places nothing of its own there.  Everything else that lives across phases
+is a compiler operand; O (MFMA accumulators only) is held in AGPRs.
 
 Hazards (the compiler does not look inside the asm): every LDS read is waited for with
-s_waitcnt before the MFMA that uses it and all reads complete inside the block; a
-transcendental result is read one instruction after it is written; a block that writes S
-ends at least 12 instructions after its last score MFMA (MFMA result -> VALU read); each
-block issues at least three instructions before its first MFMA (VALU result -> MFMA
-operand).  Code outside the blocks that reads O waits with s_nop itself.
+s_waitcnt before the MFMA that uses it and all reads complete inside the block; an LDS read
+refills a fragment buffer only two or more MFMAs after the last MFMA reading it (checked,
+also across consecutive phases); a transcendental result is read one instruction after it
+is written; a block that writes S ends at least 12 instructions after its last score MFMA
+(MFMA result -> VALU read); each block issues at least three instructions before its first
+MFMA (VALU result -> MFMA operand); an M0 write is followed by one wait state before the
+LDS-DMA load that reads it.  Code outside the blocks that reads O waits with s_nop itself.
 """
 
 from __future__ import annotations

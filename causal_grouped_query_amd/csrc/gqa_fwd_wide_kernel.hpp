@@ -1,10 +1,10 @@
 // gqa_fwd_wide_kernel.hpp -- the head-dim-128 attention forward with 64 query rows per
 // wave.
 //
-// Same operation, layouts, work decode and K/V ring as gqa_causal_fwd_kernel (the tiled
-// form of the causal GQA of the h3.c issue "Qwen text encoder: sequence exceeds Metal
-// threadgroup memory with reference video + ref images (>=150 frames)", sections "Error"
-// and "Suggested fix directions"); what changes is how a CU spends its cycles:
+// Same operation, layouts and work decode as gqa_causal_fwd_kernel (the tiled form of the
+// causal GQA of the h3.c issue "Qwen text encoder: sequence exceeds Metal threadgroup memory
+// with reference video + ref images (>=150 frames)", sections "Error" and "Suggested fix
+// directions"); what changes is how a CU spends its cycles:
 //
 //  * One workgroup = 4 waves, one per SIMD, and each wave owns two blocks of 32 query rows
 //    (64 rows).  Every K fragment and V^T fragment a wave reads from LDS is the A operand of
@@ -21,20 +21,22 @@
 //  * The running max of a row is its max over the first sub-tile; later sub-tiles are
 //    exponentiated against it, and only when a lane's 16 weights of a sub-tile sum past
 //    WEIGHT_SUM_LIMIT does the wave take the max path (C++ after the phase): raise the max
-//    of the flagged rows, rescale their O and l, and redo the sub-tile's weights.  Every
-//    decision depends on the row's own scores only.
+//    of the flagged rows (with MAX_HEADROOM), rescale their O and l, and redo the sub-tile's
+//    weights.  Every decision depends on the row's own scores only.
 //
 //  * K/V tiles go global -> LDS by DMA into a 4-stage ring, each wave loading a quarter of
 //    every tile, and the loads are issued from inside the phases, between MFMAs: the phase
 //    of sub-tile 2t issues V of tile t+2, that of 2t+1 issues K of tile t+3.  One barrier
 //    per 64-key tile: B_t follows the phase of 2t and waits for every load but the newest
-//    eight (tile t+2's), so tile t+1 is whole in LDS for the phase of 2t+1, and the stage
-//    the next loads overwrite (tile t-1's K, tile t-2's V) has been read for the last time
-//    before B_t.
+//    eight (tile t+2's), so tile t+1 is whole in LDS for the phase of 2t+1; every load goes
+//    into a stage whose last reader ran before the previous barrier.
 //
 //  * A wave whose rows end early runs the remaining phases as fill-only (the skip is a
 //    scalar branch inside the phase's assembly, so both paths share one register
 //    interface), and every wave leaves the tile loop through the same exit.
+//
+//  * O leaves through an LDS stage (the K half of the ring) so that each store writes whole
+//    256-byte rows; Q loads and O stores are non-temporal, leaving L2 to K/V.
 #pragma once
 
 #include "gqa_fwd_kernel.hpp"
@@ -287,11 +289,13 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
     }
   };
 
-  // Phase of sub-tile j >= 1, for waves with j <= j_last + 1 (wave-uniform).  K of sub-tile
-  // j+1 sits at byte offset KOFF, V of sub-tile j-1 at VOFF (stage * tile + half * sub-tile).
-  // The full phase always runs: at j = j_last its scores (of a sub-tile this wave does not
-  // need) are never read, and at j = j_last + 1 only its P.V counts.  One register interface
-  // for every sub-tile keeps the compiler's allocation of the operands stable.
+  // Phase of sub-tile j >= 1.  K of sub-tile j+1 sits at byte offset KOFF, V of sub-tile j-1
+  // at VOFF (stage * tile + half * sub-tile); f is the tile this phase helps fill, FKV whether
+  // it is that tile's V (else K), FST its stage.  For j <= j_last + 1 the whole phase runs:
+  // at j = j_last its scores (of a sub-tile this wave does not need) are never read, and at
+  // j = j_last + 1 only its P.V counts.  Past that the assembly branches to the fill loads
+  // alone.  One register interface for every sub-tile keeps the compiler's allocation of the
+  // operands stable.
   auto phase = [&](int j, auto parity, auto koff, auto voff, int f, auto fkv, auto fst)
       __attribute__((always_inline)) {
     constexpr int PAR = decltype(parity)::value;   // j & 1
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
     using I = std::integral_constant<int, 0>;
     if (t > 0) {
       // sub-tile 2t: K of 2t+1 (tile t, upper half), V of 2t-1 (tile t-1, upper half);
-      // fills V of tile t+2 into stage SN... (issued by the phase of 2(t-1)+2 = 2t)
+      // issues V of tile t+2 into stage (ST + 2) % 4, tile t-2's, last read before B_{t-1}
       phase(2 * t, std::integral_constant<int, 0>{}, std::integral_constant<int, ST * TB + SB>{},
             std::integral_constant<int, SP * TB + SB>{}, t + 2, std::integral_constant<int, 1>{},
             std::integral_constant<int, (ST + 2) % 4>{});
