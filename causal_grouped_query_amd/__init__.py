@@ -354,19 +354,32 @@ def gqa_causal_varlen_fwd(q, k, v, cu_seqlens, max_seqlen: int,
     """Causal GQA forward of a packed batch of independent sequences.
 
     q [T, Hq, D], k and v [T, Hkv, D] bf16 on the GPU; ``cu_seqlens`` an int32
-    GPU tensor [num_seqs + 1] of offsets (cu[0] = 0, cu[-1] = T);
-    ``max_seqlen`` bounds every sequence length.  Returns ``(o, lse)`` with
-    lse [Hq, T] indexed by packed token.
+    tensor [num_seqs + 1] of offsets (cu[0] = 0, cu[-1] = T), on q's device or
+    on the host; ``max_seqlen`` bounds every sequence length.  Returns
+    ``(o, lse)`` with lse [Hq, T] indexed by packed token.
+
+    Offsets on the device are not read on the host: a table that breaks those
+    rules gives unspecified rows (in particular the rows of a sequence past its
+    first ``max_seqlen`` tokens are left unwritten), never an out-of-bounds
+    access.  Offsets on the host are checked first (``H3AttnError`` with
+    ``ERR_SHAPE`` on a bad table) and then copied to q's device; device offsets
+    are checked too when ``H3ATTN_CHECK_CU_SEQLENS=1`` is set in the environment
+    (the library copies them back, one small synchronous read).
     """
     import torch
 
     _check_tensors(q, k, v)
     T, Hq, D = q.shape
     Hkv = k.shape[1]
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device.type == "cpu":
+        host = cu_seqlens.to(torch.int32).contiguous()
+        _check(check_cu_seqlens(host.numpy(), T, int(max_seqlen)))
+        cu_seqlens = host.to(q.device)
     if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 \
             or cu_seqlens.device != q.device or cu_seqlens.dim() != 1 \
             or not cu_seqlens.is_contiguous():
-        raise ValueError("h3attn: cu_seqlens must be a contiguous int32 tensor on q's device")
+        raise ValueError("h3attn: cu_seqlens must be a contiguous int32 tensor on q's device "
+                         "or on the host")
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     out, lse = _outputs(q, out, lse, return_lse)
     lib = load_library()

@@ -214,6 +214,13 @@ def test_varlen_offsets_check_under_env_switch(lib, monkeypatch):
     o2, l2 = lib.gqa_causal_varlen_fwd(qd, kd, vd, cu, 130)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # host offsets: checked by the binding, then copied to the device
+    o3, l3 = lib.gqa_causal_varlen_fwd(qd, kd, vd, cu.cpu(), 130)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    with pytest.raises(lib.H3AttnError) as err:
+        lib.gqa_causal_varlen_fwd(qd, kd, vd, cu.cpu(), 129, out=o)
+    assert err.value.status == lib.ERR_SHAPE
 
 
 def test_deterministic_and_lse_optional(lib):
