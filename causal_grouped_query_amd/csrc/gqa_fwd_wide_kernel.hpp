@@ -410,7 +410,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
   // K half of the ring (64 KB, no longer read once every wave has passed this barrier) holds
   // a [256 rows][128] bf16 stage, wave w owning rows 64w .. 64w+63; the 16-byte chunk c of
   // row r sits at chunk c ^ (r & 15), so both the row-wise writes and the chunk-wise reads
-  // below spread over all LDS banks.
+  // below spread over all LDS banks.  The last phases issued fill loads of tiles past the
+  // workgroup's last one (zeros) into K stages; every wave waits for its own before the
+  // barrier, so none can land in the stage after O is written there.
+  wait_vmem();
   __syncthreads();
   uint8_t* const ostage = reinterpret_cast<uint8_t*>(&k_lds[0][0]) + wave * 64 * 256;
   float l_tot[2];
