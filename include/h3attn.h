@@ -22,11 +22,15 @@
  * Conventions shared by every entry point:
  *   - Tensors are DEVICE pointers (memory the caller allocated on the current
  *     HIP device), dense and row-major in the shapes given; the caller owns
- *     them.  The library allocates nothing and keeps no per-call state.
+ *     them.  The library allocates no device memory (the fixed scratch array
+ *     of h3attn_gqa_causal_splitkv_fwd_noalloc is part of its code object) and
+ *     keeps no per-call state.
  *   - The call enqueues work on `hip_stream` (NULL: the null stream) and
- *     returns without waiting; the caller synchronises.
+ *     returns without waiting; the caller synchronises.  (The packed call's
+ *     opt-in offsets check, H3ATTN_CHECK_CU_SEQLENS=1, waits for its own small
+ *     copy of the offsets.)
  *   - Arguments are checked on the host before any device work.  On any
- *     nonzero status nothing was enqueued and no output byte was written.
+ *     nonzero status no kernel was enqueued and no output byte was written.
  *   - There is no limit on the sequence length other than 32-bit indexing:
  *     tokens * Hq * D < 2^31.  There is no capacity error.
  *   - Calls into the library from several host threads are safe.
