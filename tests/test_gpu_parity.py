@@ -281,3 +281,35 @@ def test_rejects_bad_arguments_on_gpu(lib):
     with pytest.raises(lib.H3AttnError) as e:
         lib.gqa_causal_fwd(q, k, k, softmax_scale=float("nan"))
     assert e.value.status == lib.ERR_SCALE
+
+
+# lengths around every boundary of the head-dim-128 kernel: 32-key sub-tiles, 64-key tiles,
+# a wave's 64/G tokens, a workgroup's 256/G tokens, and the 4-stage ring wrapping
+SWEEP_LENGTHS = sorted(set(list(range(1, 70)) + [95, 96, 97, 127, 128, 129, 191, 192, 193,
+                                                 255, 256, 257, 287, 288, 289, 511, 512, 513]))
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(16, 2), (8, 8), (8, 4), (16, 4)])
+def test_head_dim_128_length_sweep(lib, Hq, Hkv):
+    """Every length in SWEEP_LENGTHS, causal and bidirectional, against the oracle: covers
+    waves whose rows end before the workgroup's last sub-tile (fill-only phases), ragged
+    last tiles and ring wrap-around for each group size."""
+    import torch
+
+    D = 128
+    scale = workloads.default_scale(D)
+    worst = (0.0, 0.0, 0.0)
+    for S in SWEEP_LENGTHS:
+        q, k, v = normal_inputs(1000 + S, S, Hq, Hkv, D)
+        qd, kd, vd = to_device(q), to_device(k), to_device(v)
+        o, lse = lib.gqa_causal_fwd(qd, kd, vd, softmax_scale=scale)
+        ob, lb = lib.gqa_fwd(qd, kd, vd, causal=False, softmax_scale=scale)
+        torch.cuda.synchronize()
+        for (og, lg), ref, what in (((o, lse), oracle.gqa_causal(q, k, v, scale), "causal"),
+                                    ((ob, lb), oracle.gqa_bidirectional(q, k, v, scale),
+                                     "bidirectional")):
+            rel, mx, lmx = assert_close(to_f64(og), to_f64(lg), ref[0], ref[1],
+                                        f"S={S} {Hq}/{Hkv} {what}")
+            worst = tuple(max(a, b) for a, b in zip(worst, (rel, mx, lmx)))
+    print(f"[parity] sweep {Hq}/{Hkv}: worst rel_l2={worst[0]:.3e} max_abs={worst[1]:.3e} "
+          f"lse_abs={worst[2]:.3e}", flush=True)
