@@ -82,7 +82,7 @@ def copy_probe(mib: int) -> None:
 # the benchmarked kernel's source: the head-dim-128 forward (its statements, its launch shape,
 # its generated phases, and the shared parameter block / helpers it includes)
 KERNEL_SOURCES = ("gqa_fwd_wide_kernel.hpp", "tile_phases.inc", "gqa_fwd_kernel.hpp")
-KERNEL_NAME = "gqa_fwd_wide_kernel<WideConfig<128, 8>, false, true>"
+KERNEL_NAME = "gqa_fwd_wide_kernel<WideConfig<128, 8>, false, true, false>"
 # counter runs of that kernel on the benchmarked workload (trace, utilisation, HBM traffic)
 PROFILE = "gqa_fwd_wide_s10231.txt"
 

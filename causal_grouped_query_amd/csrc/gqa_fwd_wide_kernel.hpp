@@ -76,8 +76,13 @@ struct WideConfig {
 // so rows whose max keeps growing (large-logit inputs) take the max path far less often.
 constexpr float MAX_HEADROOM = 16.0f;
 
-template <class C, bool VARLEN, bool CAUSAL>
-__global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p) {
+// QPRO: the fixed-length causal forward with Q's per-head RMS norm and rotate-half RoPE
+// applied to the Q fragments in the kernel (the call h3attn_gqa_causal_qnorm_rope_fwd); its
+// LDS adds a cos/sin table of the workgroup's 256/G tokens (G = 4 and 8 fit beside the ring).
+template <class C, bool VARLEN, bool CAUSAL, bool QPRO = false>
+__global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p, QproParams qp) {
+  static_assert(!QPRO || (!VARLEN && CAUSAL), "the Q prologue instance is fixed-length causal");
+  static_assert(!QPRO || C::LDS_BYTES + C::TOK_WG * (C::D / 2) * 8 <= 160 * 1024, "LDS");
   using namespace wide::d128;
   constexpr int D = C::D, G = C::G, BN = C::BN;
   constexpr int NDS = D / 16, NDB = D / 32;
@@ -134,6 +139,37 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
     my_valid[r] = my_tok[r] < len;
   }
   const int my_head = g * G + col % G;
+
+  // ---- Q prologue, part 1: cos / sin of every (token of the block, rotation pair) into LDS.
+  // Thread t takes pair i = t mod D/2 and every (THREADS / (D/2))-th token.  theta^(-2i/D) is
+  // the host's fp64 theta^(-2/D) raised to i by squaring; the angle pos * theta^(-2i/D) is
+  // formed and reduced to [-pi, pi] in fp64 (positions reach 10^4-10^5 rad), then cos / sin
+  // are taken in fp32.  Read after the prologue's barrier.
+  [[maybe_unused]] float2* qcs = nullptr;
+  if constexpr (QPRO) {
+    constexpr int HALF = D / 2;
+    __shared__ float2 qcs_lds[C::TOK_WG * HALF];
+    qcs = qcs_lds;
+    if (qp.rope) {
+      const int i = tid % HALF;
+      double inv_freq = 1.0, power = qp.inv_freq_step;
+      for (int b = i; b != 0; b >>= 1) {
+        if (b & 1) inv_freq *= power;
+        power *= power;
+      }
+      for (int tt = tid / HALF; tt < C::TOK_WG; tt += C::THREADS / HALF) {
+        const int tok = q0 + tt;
+        float sn = 0.0f, cs = 1.0f;
+        if (tok < len) {
+          const double pos = qp.positions ? (double)qp.positions[start + tok] : (double)tok;
+          const double a = pos * inv_freq;
+          const double r = a - 6.283185307179586476925 * rint(a * 0.159154943091895335768883);
+          sincosf((float)r, &sn, &cs);
+        }
+        qcs[tt * HALF + i] = make_float2(cs, sn);
+      }
+    }
+  }
 
   // ---- Q^T fragments of both row blocks (B operands), resident for the whole kernel
   bf16x8 qf[2][NDS];
@@ -343,6 +379,50 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
   wait_vmem();
   if (2 < n_tiles) fill_tile(2, k_lds[2], v_lds[2]);
   __syncthreads();
+  if constexpr (QPRO) {
+    // Q prologue, part 2, on this lane's fragments of both row blocks: elements
+    // 16*ds + 8*half + 0..7 of the row; element d and its rotation partner d + D/2 sit in
+    // fragments ds and ds + NDS/2 of the same lane, and lanes l and l^32 hold the two halves
+    // of one row (the norm's sum of squares is one swap across the pair).
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      f32x8 x[NDS];
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) x[ds] = __builtin_convertvector(qf[r][ds], f32x8);
+      if (qp.q_weight != nullptr) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+          for (int t = 0; t < 8; ++t) ss += x[ds][t] * x[ds][t];
+        ss = pair_sum(ss);
+        const float inv = 1.0f / __builtin_sqrtf(ss / (float)D + qp.q_eps);
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+          const f32x8 w = __builtin_convertvector(
+              __builtin_bit_cast(bf16x8, *(const u32x4*)(qp.q_weight + 16 * ds + 8 * half)),
+              f32x8);
+          x[ds] = x[ds] * inv * w;
+        }
+      }
+      if (qp.rope) {
+        const float2* row = qcs + (wave * C::TOK_W + r * C::TOK_RB + col / G) * (D / 2);
+#pragma unroll
+        for (int ds = 0; ds < NDS / 2; ++ds)
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float2 cs = row[16 * ds + 8 * half + t];
+            const float lo = x[ds][t], hi = x[ds + NDS / 2][t];
+            x[ds][t] = lo * cs.x - hi * cs.y;
+            x[ds + NDS / 2][t] = hi * cs.x + lo * cs.y;
+          }
+      }
+      if (my_valid[r]) {
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) qf[r][ds] = __builtin_convertvector(x[ds], bf16x8);
+      }
+    }
+  }
   if (0 <= j_last) {
     phase_scores<0, 0>(qf, s_[0], ka, fx);
     mask(s_[0], 0);
@@ -465,15 +545,16 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
 // Host side: one workgroup per (query block, KV head, sequence).  Returns the launch's HIP
 // error; hipSuccess without a launch for an empty grid, hipErrorInvalidConfiguration when the
 // grid would not fit the 32-bit x dimension.
-template <int G, bool VARLEN, bool CAUSAL>
-inline hipError_t launch_gqa_fwd_wide(FwdParams p, hipStream_t stream) {
+template <int G, bool VARLEN, bool CAUSAL, bool QPRO = false>
+inline hipError_t launch_gqa_fwd_wide(FwdParams p, hipStream_t stream,
+                                      const QproParams& qp = QproParams{}) {
   using C = WideConfig<128, G>;
   p.n_qblk = (p.seq_len + C::TOK_WG - 1) / C::TOK_WG;
   const long long blocks = (long long)p.n_qblk * p.hkv * p.num_seqs;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((gqa_fwd_wide_kernel<C, VARLEN, CAUSAL>), dim3((unsigned)blocks),
-                     dim3(C::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((gqa_fwd_wide_kernel<C, VARLEN, CAUSAL, QPRO>), dim3((unsigned)blocks),
+                     dim3(C::THREADS), 0, stream, p, qp);
   return hipGetLastError();
 }
 

@@ -134,6 +134,13 @@ int launch_qpro(const FwdParams& p, const h3attn::QproParams& qp, hipStream_t st
   return hipGetLastError() == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
 }
 
+template <int G>
+int launch_wide_qpro(const FwdParams& p, const h3attn::QproParams& qp, hipStream_t stream) {
+  const hipError_t e = h3attn::launch_gqa_fwd_wide<G, false, true, true>(p, stream, qp);
+  if (e == hipErrorInvalidConfiguration) return H3ATTN_ERR_SHAPE;
+  return e == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
+}
+
 // (D, G) pairs with a qpro instance: at D = 128 and G = 1 the table (256 tokens) would not
 // fit beside the K/V ring.
 bool qpro_supported(int D, int G) { return D == 64 || G != 1; }
@@ -142,9 +149,11 @@ int dispatch_qpro(int D, int G, const FwdParams& p, const h3attn::QproParams& qp
                   hipStream_t stream) {
   if (D == 128) {
     switch (G) {
+      // G = 4 and 8: the 64-row kernel (its table fits beside the 128 KB ring); G = 2: the
+      // 32-row kernel (96 KB ring + a 64 KB table)
       case 2: return launch_qpro<128, 2>(p, qp, stream);
-      case 4: return launch_qpro<128, 4>(p, qp, stream);
-      case 8: return launch_qpro<128, 8>(p, qp, stream);
+      case 4: return launch_wide_qpro<4>(p, qp, stream);
+      case 8: return launch_wide_qpro<8>(p, qp, stream);
     }
   } else if (D == 64) {
     switch (G) {
