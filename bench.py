@@ -231,6 +231,18 @@ def reference(oracle, inp, w, tokens):
                                     tokens=tokens)
 
 
+def host_cpu_model() -> str | None:
+    """The host CPU's model name (first processor in /proc/cpuinfo), None where unknown."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(inp, w, target_s: float):
     """fp64 oracle throughput on a bounded sample of query tokens (all heads)."""
     import oracle
@@ -266,6 +278,7 @@ def cpu_baseline(inp, w, target_s: float):
         "value": flop / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.threads(),
+        "cpu_model": host_cpu_model(),
         "kind": "oracle",
         "sample": (f"{n} query tokens drawn uniformly from the {w.name} workload, all "
                    f"{w.n_q_heads} heads, full {'causal ' if w.causal else ''}rows; "
@@ -340,7 +353,8 @@ def bench_prologue(args, w, inp, torch, h3):
                                       "pass": bool(worst <= 1.0)}
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = {"value": nbytes / dt / 1e9, "unit": "GB/s",
-                                      "cores": oracle.threads(), "kind": "oracle",
+                                      "cores": oracle.threads(),
+                                      "cpu_model": host_cpu_model(), "kind": "oracle",
                                       "sample": f"the full Q and K of {w.name} ({elems} elements) "
                                                 f"in {dt:.1f} s"}
     print(json.dumps(result), flush=True)
@@ -484,6 +498,7 @@ def bench_pool(args, w, torch, h3):
                                       "pass": bool(worst <= 1.0)}
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1,
+                                      "cpu_model": host_cpu_model(),
                                       "kind": "oracle", "sample": f"the full [{T}, {C}] prompt, "
                                       f"numpy float64 loops, in {dt:.1f} s"}
     print(json.dumps(result), flush=True)
