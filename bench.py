@@ -5,7 +5,8 @@
 A step is one call of the forward (one kernel launch) over the whole
 workload, inputs already resident in HBM.  Prints ONE JSON line with the
 throughput (causal FLOP / s: 4*D per kept (query, key) pair and query head),
-the roofline of the kernel, an oracle-match check on sampled query tokens of
+the roofline of the kernel (with the clock it ran at and the matrix-core and
+exponential ceilings measured at that occupancy), an oracle-match check on sampled query tokens of
 the benchmarked output, and the fp64 CPU oracle's own throughput on a bounded
 sample of the same workload.  Progress goes to stderr.
 """
@@ -60,6 +61,8 @@ def parse():
                     help="target wall time of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the oracle-match sample")
+    ap.add_argument("--no-calib", action="store_true",
+                    help="skip the matrix-core and exponential calibration loops")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -229,6 +232,59 @@ def reference(oracle, inp, w, tokens):
         return oracle.gqa_bidirectional(inp["q"], inp["k"], inp["v"], w.scale, tokens=tokens)
     return oracle.gqa_causal_varlen(inp["q"], inp["k"], inp["v"], w.cu_seqlens, w.scale,
                                     tokens=tokens)
+
+
+def calibration_loops(stream, achieved_tflops: float, settle_s: float = 0.3,
+                      launches: int = 60, iters: int = 4096) -> dict:
+    """The matrix-core and exponential ceilings at the clock the GPU holds
+    (h3attn_calib_loop, one wave per SIMD, the attention kernel's occupancy).  Each loop
+    first runs untimed for settle_s so the clock settles to its own load, then `launches`
+    launches are timed with events; the in-kernel stamps of the last one give the cycles
+    per instruction and the clock."""
+    import torch
+
+    import causal_grouped_query_amd as h3
+
+    ncu = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    stamps = torch.zeros((ncu * 4, 4), dtype=torch.int64, device="cuda")
+    sink = torch.empty(ncu * 256, dtype=torch.float32, device="cuda")
+    out = {}
+    for kind, name, per_iter in ((h3.CALIB_MFMA, "mfma_loop", 8), (h3.CALIB_EXP, "exp_loop", 16)):
+        def run():
+            return h3.calib_loop(kind, ncu, iters, stream=stream, stamps=stamps, sink=sink)[1]
+
+        t = time.perf_counter()
+        while time.perf_counter() - t < settle_s:
+            for _ in range(10):
+                run()
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(launches):
+            khz = run()
+        b.record(stream)
+        b.synchronize()
+        seconds = a.elapsed_time(b) * 1e-3 / launches
+        st = stamps.cpu().numpy().astype(np.float64)
+        cycles, ticks = st[:, 1] - st[:, 0], st[:, 3] - st[:, 2]
+        ghz = float(np.median(cycles / (ticks / (khz * 1e3)))) / 1e9 if khz > 0 else None
+        per_instr = float(np.median(cycles)) / (iters * per_iter)
+        waves = ncu * 4
+        entry = {"cycles_per_instruction": round(per_instr, 2),
+                 "clock_ghz": round(ghz, 3) if ghz else None,
+                 "launch_ms": round(seconds * 1e3, 4), "waves_per_simd": 1,
+                 "workgroups": ncu, "iterations": iters}
+        if kind == h3.CALIB_MFMA:
+            tflops = waves * iters * per_iter * 32768 / seconds / 1e12
+            entry.update({"instruction": "v_mfma_f32_32x32x16_bf16, random bf16 operands",
+                          "tflops": round(tflops, 1),
+                          "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+                          "kernel_frac_of_loop": round(achieved_tflops / tflops, 4)})
+        else:
+            entry.update({"instruction": "v_exp_f32",
+                          "g_exp_per_s": round(waves * 64 * iters * per_iter / seconds / 1e9, 1)})
+        out[name] = entry
+    return out
 
 
 def host_cpu_model() -> str | None:
@@ -603,6 +659,14 @@ def main():
     avg_launch_ms = float(per_launch.mean())
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
 
+    calib = None
+    if not args.no_calib:
+        try:
+            calib = calibration_loops(stream, achieved)
+            log(f"calibration loops: {calib}")
+        except Exception as e:  # reported in the line; the measurement above stands
+            calib = {"error": f"{type(e).__name__}: {e}"}
+
     primary = w.name == workloads.PRIMARY and args.path == "fused"
     # MFMA peak at the clock the part actually ran: 256 CU x 4096 bf16 flop/clk x f
     f_ghz = clock["mhz_mean"] / 1e3 if clock.get("mhz_mean") else None
@@ -663,6 +727,7 @@ def main():
             "avg_launch_ms": round(avg_launch_ms, 5),
             "algorithmic_flop_per_launch": flop,
             "shader_clock": clock,
+            **({"calibration": calib} if calib is not None else {}),
         },
     }
 

@@ -35,12 +35,13 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # fixed scratch of h3attn_gqa_causal_splitkv_
 
 NONCAUSAL, O_HEAD_MAJOR = 1, 2   # flags of h3attn_gqa_fwd
 PROLOGUE_ROPE = 1                # flag of h3attn_qk_norm_rope
+CALIB_MFMA, CALIB_EXP = 0, 1     # kinds of h3attn_calib_loop
 
 EXPORTED = ("h3attn_gqa_causal_fwd", "h3attn_gqa_fwd", "h3attn_gqa_causal_varlen_fwd",
             "h3attn_gqa_causal_splitkv_fwd", "h3attn_gqa_causal_splitkv_workspace_bytes",
             "h3attn_qk_norm_rope", "h3attn_gqa_causal_qnorm_rope_fwd", "h3attn_pool_tokens",
             "h3attn_pool_tokens_out_len", "h3attn_check_cu_seqlens",
-            "h3attn_gqa_causal_splitkv_fwd_noalloc",
+            "h3attn_gqa_causal_splitkv_fwd_noalloc", "h3attn_calib_loop",
             "h3attn_status_string", "h3attn_version",
             "h3attn_lds_bytes")
 
@@ -107,6 +108,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         lib.h3attn_gqa_causal_splitkv_fwd_noalloc.restype = i32
         lib.h3attn_check_cu_seqlens.argtypes = [vp, i32, i32, i32]
         lib.h3attn_check_cu_seqlens.restype = i32
+        lib.h3attn_calib_loop.argtypes = [i32, i32, i32, vp, vp, ctypes.POINTER(i32), vp]
+        lib.h3attn_calib_loop.restype = i32
         if path == LIBRARY:
             _lib = lib
         return lib
@@ -320,6 +323,36 @@ def check_cu_seqlens(cu_seqlens, total_tokens: int, max_seqlen: int) -> int:
                                                       int(max_seqlen)))
 
 
+def calib_loop(kind: int, n_workgroups: int, iters: int, stream=None, device=None,
+               stamps=None, sink=None):
+    """Enqueue one calibration loop (CALIB_MFMA or CALIB_EXP; see h3attn_calib_loop) and
+    return (stamps, wall_clock_khz): stamps is an int64 GPU tensor [n_workgroups * 4, 4]
+    (per wave: shader-clock counter before / after its loop, constant-rate counter before /
+    after), filled when the stream reaches the launch; wall_clock_khz is the rate of the
+    constant-rate counter.  stamps and sink (float32 [n_workgroups * 256]) may be passed in
+    to reuse them across calls."""
+    import torch
+
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    n = int(n_workgroups)
+    if stamps is None:
+        stamps = torch.zeros((n * 4, 4), dtype=torch.int64, device=device)
+    if sink is None:
+        sink = torch.empty(n * 256, dtype=torch.float32, device=device)
+    if stamps.dtype != torch.int64 or not stamps.is_contiguous() or stamps.numel() < n * 16 \
+            or sink.dtype != torch.float32 or not sink.is_contiguous() or sink.numel() < n * 256:
+        raise ValueError("h3attn: stamps must be contiguous int64 with n_workgroups * 16 "
+                         "elements, sink contiguous float32 with n_workgroups * 256")
+    khz = ctypes.c_int(0)
+    _check(load_library().h3attn_calib_loop(int(kind), int(n_workgroups), int(iters),
+                                            stamps.data_ptr(), sink.data_ptr(),
+                                            ctypes.byref(khz), _stream_handle(stream, device)))
+    if stream is not None:   # both buffers stay reserved until that stream's work is done
+        stamps.record_stream(stream)
+        sink.record_stream(stream)
+    return stamps, int(khz.value)
+
+
 def pool_tokens_out_len(T: int, begin: int, end: int, factor: int) -> int:
     """Length of :func:`pool_tokens`'s output (-1 for invalid arguments)."""
     return int(load_library().h3attn_pool_tokens_out_len(int(T), int(begin), int(end),
@@ -456,4 +489,4 @@ __all__ = ["gqa_causal_fwd", "gqa_fwd", "gqa_causal_varlen_fwd", "gqa_causal_spl
            "splitkv_workspace_bytes", "status_string", "version", "lds_bytes", "load_library",
            "H3AttnError", "LIBRARY", "EXPORTED", "MAX_SPLITS", "NONCAUSAL", "O_HEAD_MAJOR",
            "qk_norm_rope", "gqa_causal_qnorm_rope_fwd", "PROLOGUE_ROPE", "pool_tokens",
-           "pool_tokens_out_len"]
+           "pool_tokens_out_len", "calib_loop", "CALIB_MFMA", "CALIB_EXP"]

@@ -15,9 +15,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", "h3attn.hip")]
-HEADERS = [os.path.join(PKG, "csrc", "gqa_fwd_kernel.hpp"), os.path.join(PKG, "csrc", "gqa_fwd_body.inc"),
-           os.path.join(PKG, "csrc", "gqa_fwd_wide_kernel.hpp"), os.path.join(PKG, "csrc", "tile_phases.inc"),
-           os.path.join(ROOT, "include", "h3attn.h")]
+HEADERS = [os.path.join(PKG, "csrc", n) for n in (
+    "calib_kernel.hpp", "gqa_fwd_kernel.hpp", "gqa_fwd_body.inc", "gqa_fwd_wide_kernel.hpp",
+    "tile_phases.inc")] + [os.path.join(ROOT, "include", "h3attn.h")]
 LIBRARY = os.path.join(PKG, "libh3attn.so")
 ARCH = "gfx950"
 

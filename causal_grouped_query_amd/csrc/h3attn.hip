@@ -17,6 +17,7 @@
 #include <mutex>
 #include <vector>
 
+#include "calib_kernel.hpp"
 #include "gqa_fwd_kernel.hpp"
 #include "gqa_fwd_wide_kernel.hpp"
 #include "gqa_merge_kernel.hpp"
@@ -530,6 +531,33 @@ int h3attn_gqa_causal_splitkv_fwd_noalloc(const void* q, const void* k, const vo
   if (ws == nullptr) return H3ATTN_ERR_DEVICE;
   return h3attn_gqa_causal_splitkv_fwd(q, k, v, o, lse, S, Hq, Hkv, D, softmax_scale, num_splits,
                                        ws, H3ATTN_NOALLOC_SCRATCH_BYTES, hip_stream);
+}
+
+int h3attn_calib_loop(int kind, int n_workgroups, int iters, uint64_t* stamps, float* sink,
+                      int* wall_clock_khz, void* hip_stream) {
+  if (!stamps || !sink) return H3ATTN_ERR_NULL;
+  if (n_workgroups < 1 || n_workgroups > 65535 || iters < 1 || iters > (1 << 24))
+    return H3ATTN_ERR_SHAPE;
+  if (kind != H3ATTN_CALIB_MFMA && kind != H3ATTN_CALIB_EXP) return H3ATTN_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(stamps) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+    return H3ATTN_ERR_ALIGN;
+  if (!device_ok()) return H3ATTN_ERR_DEVICE;
+  if (wall_clock_khz) {
+    int dev = -1, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+      return H3ATTN_ERR_DEVICE;
+    *wall_clock_khz = khz;
+  }
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (kind == H3ATTN_CALIB_MFMA)
+    hipLaunchKernelGGL((h3attn::calib_loop_kernel<0>), dim3(n_workgroups),
+                       dim3(h3attn::CALIB_THREADS), 0, st, stamps, sink, iters);
+  else
+    hipLaunchKernelGGL((h3attn::calib_loop_kernel<1>), dim3(n_workgroups),
+                       dim3(h3attn::CALIB_THREADS), 0, st, stamps, sink, iters);
+  return hipGetLastError() == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
 }
 
 const char* h3attn_status_string(int status) {

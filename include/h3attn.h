@@ -286,6 +286,34 @@ H3ATTN_API int h3attn_pool_tokens(const void* x, void* out, int T, int C, int be
 /* Output length of h3attn_pool_tokens, or -1 for invalid arguments. */
 H3ATTN_API int h3attn_pool_tokens_out_len(int T, int begin, int end, int factor);
 
+/*
+ * Calibration loops (not a step of the attention): the sustained rate of the two
+ * resources the attention kernel's inner loop is built from, measured on the running GPU
+ * at the clock it holds, so that the kernel's throughput can be set against what the chip
+ * reaches as well as against its published peak.
+ *   kind H3ATTN_CALIB_MFMA: each wave issues iters * 8 v_mfma_f32_32x32x16_bf16 (32768
+ *     flop each) on fixed pseudo-random bf16 operands (eight A and eight B fragments, so
+ *     consecutive MFMAs differ in both) into four accumulators;
+ *   kind H3ATTN_CALIB_EXP: each wave issues iters * 16 v_exp_f32 on sixteen independent
+ *     fp32 values.
+ * n_workgroups workgroups of 256 threads (four waves); each reserves 96 KB of LDS, so no
+ * compute unit holds two of them: with n_workgroups equal to the number of compute units
+ * every SIMD runs one wave, the attention kernel's occupancy.
+ *   stamps  DEVICE uint64 [n_workgroups * 4][4]: per wave, the shader-clock counter
+ *           (s_memtime) before and after its loop, then the constant-rate counter
+ *           (s_memrealtime) before and after;
+ *   sink    DEVICE float [n_workgroups * 256]: one value per thread that keeps the loop's
+ *           results live (no meaning otherwise);
+ *   wall_clock_khz  HOST int or NULL: receives the rate of the constant-rate counter.
+ * 1 <= n_workgroups <= 65535 and 1 <= iters <= 2^24 (else H3ATTN_ERR_SHAPE); another kind
+ * is H3ATTN_ERR_UNSUPPORTED; stamps and sink non-NULL (H3ATTN_ERR_NULL), 8- and 4-byte
+ * aligned (H3ATTN_ERR_ALIGN).  Enqueued on hip_stream like the other calls.
+ */
+#define H3ATTN_CALIB_MFMA 0
+#define H3ATTN_CALIB_EXP 1
+H3ATTN_API int h3attn_calib_loop(int kind, int n_workgroups, int iters, uint64_t* stamps,
+                                 float* sink, int* wall_clock_khz, void* hip_stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 H3ATTN_API const char* h3attn_status_string(int status);
 
