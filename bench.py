@@ -239,8 +239,8 @@ def calibration_loops(stream, achieved_tflops: float, settle_s: float = 0.3,
     """The matrix-core and exponential ceilings at the clock the GPU holds
     (h3attn_calib_loop, one wave per SIMD, the attention kernel's occupancy).  Each loop
     first runs untimed for settle_s so the clock settles to its own load, then `launches`
-    launches are timed with events; the in-kernel stamps of the last one give the cycles
-    per instruction and the clock."""
+    launches are timed with events; the in-kernel stamps of the last one give the clock
+    and each wave's own cycles per instruction."""
     import torch
 
     import causal_grouped_query_amd as h3
@@ -249,7 +249,9 @@ def calibration_loops(stream, achieved_tflops: float, settle_s: float = 0.3,
     stamps = torch.zeros((ncu * 4, 4), dtype=torch.int64, device="cuda")
     sink = torch.empty(ncu * 256, dtype=torch.float32, device="cuda")
     out = {}
-    for kind, name, per_iter in ((h3.CALIB_MFMA, "mfma_loop", 8), (h3.CALIB_EXP, "exp_loop", 16)):
+    for kind, name, per_iter in ((h3.CALIB_MFMA, "mfma_loop", 8),
+                                 (h3.CALIB_MFMA_ZERO, "mfma_loop_zero_operands", 8),
+                                 (h3.CALIB_EXP, "exp_loop", 16)):
         def run():
             return h3.calib_loop(kind, ncu, iters, stream=stream, stamps=stamps, sink=sink)[1]
 
@@ -268,9 +270,13 @@ def calibration_loops(stream, achieved_tflops: float, settle_s: float = 0.3,
         st = stamps.cpu().numpy().astype(np.float64)
         cycles, ticks = st[:, 1] - st[:, 0], st[:, 3] - st[:, 2]
         ghz = float(np.median(cycles / (ticks / (khz * 1e3)))) / 1e9 if khz > 0 else None
-        per_instr = float(np.median(cycles)) / (iters * per_iter)
         waves = ncu * 4
-        entry = {"cycles_per_instruction": round(per_instr, 2),
+        # per SIMD, from the event-timed launches at the stamped clock (launch overhead
+        # included); and each wave's own loop, from its stamps
+        per_simd = (ghz * 1e9 * seconds / (iters * per_iter)) if ghz else None
+        entry = {"cycles_per_instruction_per_simd": round(per_simd, 2) if per_simd else None,
+                 "wave_loop_cycles_per_instruction":
+                     round(float(np.median(cycles)) / (iters * per_iter), 2),
                  "clock_ghz": round(ghz, 3) if ghz else None,
                  "launch_ms": round(seconds * 1e3, 4), "waves_per_simd": 1,
                  "workgroups": ncu, "iterations": iters}
@@ -280,6 +286,12 @@ def calibration_loops(stream, achieved_tflops: float, settle_s: float = 0.3,
                           "tflops": round(tflops, 1),
                           "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
                           "kernel_frac_of_loop": round(achieved_tflops / tflops, 4)})
+        elif kind == h3.CALIB_MFMA_ZERO:
+            tflops = waves * iters * per_iter * 32768 / seconds / 1e12
+            entry.update({"instruction": "v_mfma_f32_32x32x16_bf16, all-zero operands "
+                                         "(no datapath toggling; not a ceiling for real data)",
+                          "tflops": round(tflops, 1),
+                          "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)})
         else:
             entry.update({"instruction": "v_exp_f32",
                           "g_exp_per_s": round(waves * 64 * iters * per_iter / seconds / 1e9, 1)})

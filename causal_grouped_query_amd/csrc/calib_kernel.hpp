@@ -8,7 +8,9 @@
 // instructions and one wave per SIMD (the attention kernel's occupancy):
 //   KIND 0: eight MFMAs per iteration into four accumulators, the A and B fragments
 //           fixed pseudo-random bf16 values (eight of each, so consecutive MFMAs differ
-//           in both operands and the datapath toggles as it does on real data);
+//           in both operands and the datapath toggles as it does on real data), or, with
+//           operand_mask 0, all-zero operands (the same instructions with a datapath that
+//           does not toggle: the clock difference between the two is the power limit);
 //   KIND 1: sixteen independent v_exp_f32 per iteration (x <- 2^-x keeps x in (0, 1]).
 // Each wave records the shader-clock counter (s_memtime) and the constant-rate counter
 // (s_memrealtime) around its loop (in asm that waits for the values and takes the loop's
@@ -44,7 +46,8 @@ __device__ __forceinline__ unsigned short calib_bf16_bits(unsigned h) {
 
 template <int KIND>
 __global__ __launch_bounds__(CALIB_THREADS, 1) void calib_loop_kernel(uint64_t* stamps,
-                                                                     float* sink, int iters) {
+                                                                     float* sink, int iters,
+                                                                     unsigned operand_mask) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
   typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -65,8 +68,8 @@ __global__ __launch_bounds__(CALIB_THREADS, 1) void calib_loop_kernel(uint64_t* 
       u16x8 ua, ub;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        ua[e] = calib_bf16_bits(calib_mix(gid * 128u + i * 8u + e));
-        ub[e] = calib_bf16_bits(calib_mix(gid * 128u + 64u + i * 8u + e));
+        ua[e] = calib_bf16_bits(calib_mix(gid * 128u + i * 8u + e)) & operand_mask;
+        ub[e] = calib_bf16_bits(calib_mix(gid * 128u + 64u + i * 8u + e)) & operand_mask;
       }
       a[i] = __builtin_bit_cast(bf16x8, ua);
       b[i] = __builtin_bit_cast(bf16x8, ub);

@@ -538,7 +538,8 @@ int h3attn_calib_loop(int kind, int n_workgroups, int iters, uint64_t* stamps, f
   if (!stamps || !sink) return H3ATTN_ERR_NULL;
   if (n_workgroups < 1 || n_workgroups > 65535 || iters < 1 || iters > (1 << 24))
     return H3ATTN_ERR_SHAPE;
-  if (kind != H3ATTN_CALIB_MFMA && kind != H3ATTN_CALIB_EXP) return H3ATTN_ERR_UNSUPPORTED;
+  if (kind != H3ATTN_CALIB_MFMA && kind != H3ATTN_CALIB_EXP && kind != H3ATTN_CALIB_MFMA_ZERO)
+    return H3ATTN_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(stamps) & 7u) != 0 ||
       (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
     return H3ATTN_ERR_ALIGN;
@@ -551,12 +552,13 @@ int h3attn_calib_loop(int kind, int n_workgroups, int iters, uint64_t* stamps, f
     *wall_clock_khz = khz;
   }
   const hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  if (kind == H3ATTN_CALIB_MFMA)
-    hipLaunchKernelGGL((h3attn::calib_loop_kernel<0>), dim3(n_workgroups),
-                       dim3(h3attn::CALIB_THREADS), 0, st, stamps, sink, iters);
-  else
+  if (kind == H3ATTN_CALIB_EXP)
     hipLaunchKernelGGL((h3attn::calib_loop_kernel<1>), dim3(n_workgroups),
-                       dim3(h3attn::CALIB_THREADS), 0, st, stamps, sink, iters);
+                       dim3(h3attn::CALIB_THREADS), 0, st, stamps, sink, iters, 0xFFFFu);
+  else   // one instance for both operand sets: the mask is a run-time value
+    hipLaunchKernelGGL((h3attn::calib_loop_kernel<0>), dim3(n_workgroups),
+                       dim3(h3attn::CALIB_THREADS), 0, st, stamps, sink, iters,
+                       kind == H3ATTN_CALIB_MFMA ? 0xFFFFu : 0u);
   return hipGetLastError() == hipSuccess ? H3ATTN_OK : H3ATTN_ERR_LAUNCH;
 }
 

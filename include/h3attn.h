@@ -294,6 +294,9 @@ H3ATTN_API int h3attn_pool_tokens_out_len(int T, int begin, int end, int factor)
  *   kind H3ATTN_CALIB_MFMA: each wave issues iters * 8 v_mfma_f32_32x32x16_bf16 (32768
  *     flop each) on fixed pseudo-random bf16 operands (eight A and eight B fragments, so
  *     consecutive MFMAs differ in both) into four accumulators;
+ *   kind H3ATTN_CALIB_MFMA_ZERO: the same MFMA loop on all-zero operands (a datapath that
+ *     does not toggle draws less power; the clock difference to H3ATTN_CALIB_MFMA shows
+ *     how much the power limit sets the rate on real data);
  *   kind H3ATTN_CALIB_EXP: each wave issues iters * 16 v_exp_f32 on sixteen independent
  *     fp32 values.
  * n_workgroups workgroups of 256 threads (four waves); each reserves 96 KB of LDS, so no
@@ -311,6 +314,7 @@ H3ATTN_API int h3attn_pool_tokens_out_len(int T, int begin, int end, int factor)
  */
 #define H3ATTN_CALIB_MFMA 0
 #define H3ATTN_CALIB_EXP 1
+#define H3ATTN_CALIB_MFMA_ZERO 2
 H3ATTN_API int h3attn_calib_loop(int kind, int n_workgroups, int iters, uint64_t* stamps,
                                  float* sink, int* wall_clock_khz, void* hip_stream);
 

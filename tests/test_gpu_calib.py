@@ -29,7 +29,8 @@ def _announce(request):
     yield
 
 
-@pytest.mark.parametrize("kind,per_iter,lo,hi", [(0, 8, 30.0, 80.0), (1, 16, 2.0, 64.0)])
+@pytest.mark.parametrize("kind,per_iter,lo,hi", [(0, 8, 30.0, 80.0), (2, 8, 30.0, 80.0),
+                                                 (1, 16, 2.0, 64.0)])
 def test_calib_loop_stamps(h3, kind, per_iter, lo, hi):
     import torch
 
