@@ -332,16 +332,22 @@ def cpu_baseline(inp, w, target_s: float):
         reference(oracle, inp, w, tokens)
         return time.perf_counter() - t0
 
-    calib = rng.integers(0, T, size=4)
+    calib = rng.integers(0, T, size=16)
     dt = run(calib)
     rate = 4 * w.head_dim * w.n_q_heads * pair_count(calib) / max(dt, 1e-6)   # flop/s
     per_token = 4 * w.head_dim * w.n_q_heads * (T / len(w.seqlens)) / (2 if w.causal else 1)
-    n = int(np.clip(target_s * rate / per_token, 8, T))
-    tokens = np.sort(rng.integers(0, T, size=n))
-    log(f"cpu baseline: {n} sampled query tokens x {w.n_q_heads} heads "
-        f"(~{n * per_token / rate:.1f} s expected)")
-    dt = run(tokens)
-    flop = 4 * w.head_dim * w.n_q_heads * pair_count(tokens)
+    # batches of uniformly drawn tokens until about target_s of oracle time is spent (the
+    # first estimate of the rate comes from a few tokens and can be off by a few times)
+    n, dt, flop = 0, 0.0, 0
+    while dt < 0.8 * target_s and n < T:
+        m = int(np.clip((target_s - dt) * rate / per_token, 8, T - n))
+        batch = np.sort(rng.integers(0, T, size=m))
+        log(f"cpu baseline: {m} sampled query tokens x {w.n_q_heads} heads "
+            f"(~{m * per_token / rate:.1f} s expected)")
+        dt += run(batch)
+        flop += 4 * w.head_dim * w.n_q_heads * pair_count(batch)
+        n += m
+        rate = flop / max(dt, 1e-6)
     return {
         "value": flop / dt / 1e12,
         "unit": "TFLOP/s",
