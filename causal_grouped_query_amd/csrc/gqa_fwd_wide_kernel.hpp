@@ -18,11 +18,12 @@
 //    (exp2, bf16 weights, fp32 sums) issues between the score MFMAs of sub-tile j+1 and the
 //    P.V MFMAs of sub-tile j-1, so the wave's own VALU work fills the gaps of its MFMAs.
 //
-//  * The running max of a row is its max over the first sub-tile; later sub-tiles are
-//    exponentiated against it, and only when a lane's 16 weights of a sub-tile sum past
-//    WEIGHT_SUM_LIMIT does the wave take the max path (C++ after the phase): raise the max
-//    of the flagged rows (with MAX_HEADROOM), rescale their O and l, and redo the sub-tile's
-//    weights.  Every decision depends on the row's own scores only.
+//  * The running max of a row starts INIT_HEADROOM above its max over the first sub-tile;
+//    later sub-tiles are exponentiated against it, and only when a lane's 16 weights of a
+//    sub-tile sum past WIDE_WEIGHT_SUM_LIMIT (or are not finite) does the wave take the max
+//    path (C++ after the phase): raise the max of the flagged rows (to MAX_HEADROOM above
+//    the sub-tile's max), rescale their O and l, and redo the sub-tile's weights.  Every
+//    decision depends on the row's own scores only.
 //
 //  * K/V tiles go global -> LDS by DMA into a 4-stage ring, each wave loading a quarter of
 //    every tile, and the loads are issued from inside the phases, between MFMAs: the phase
@@ -70,11 +71,20 @@ struct WideConfig {
   static_assert(TILE_PIECES % NW == 0, "tile fill divides over waves");
 };
 
-// log2 units added to a row's running max when the max path raises it.  After a raise the
-// row's largest weight is 2^-16, and the next raise needs a key scoring about 28 log2 units
-// higher (16 of headroom, 12 for one weight to push a lane's 16-weight sum past the limit),
-// so rows whose max keeps growing (large-logit inputs) take the max path far less often.
-constexpr float MAX_HEADROOM = 16.0f;
+// The lazy max in log2 units.  The max path is rare but costs a wave ~1000 cycles, and the
+// other waves of the workgroup wait for it at the next barrier, so the running max is kept
+// well above the scores seen: it starts INIT_HEADROOM above the first sub-tile's max, a
+// raise puts it MAX_HEADROOM above the raising sub-tile's max, and a raise is needed only
+// once a lane's 16 weights sum past WIDE_WEIGHT_SUM_LIMIT, i.e. once a key scores about
+// 84 log2 units above the first sub-tile's max (68 after a raise).  Ranges: a weight is at
+// most 2^40; one below 2^-126 (a key more than 78 log2 units under the row's largest
+// score) may be flushed to zero, which moves O and l by less than 2^-78 relative; a lane's
+// sum l stays below 2^40 per sub-tile, so below 2^53 over 2^13 sub-tiles (262144 keys), and
+// O stays finite for |V| < 2^74.  Scaling every weight by a power of two changes neither
+// O = acc / l nor LSE = m + log2 l.
+constexpr float INIT_HEADROOM = 48.0f;
+constexpr float MAX_HEADROOM = 32.0f;
+constexpr float WIDE_WEIGHT_SUM_LIMIT = 1099511627776.0f;   // 2^40
 
 // QPRO: the fixed-length causal forward with Q's per-head RMS norm and rotate-half RoPE
 // applied to the Q fragments in the kernel (the call h3attn_gqa_causal_qnorm_rope_fwd); its
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
     asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const uint64_t flagged = __builtin_amdgcn_ballot_w64(!(ls[r] <= WEIGHT_SUM_LIMIT));
+      const uint64_t flagged = __builtin_amdgcn_ballot_w64(!(ls[r] <= WIDE_WEIGHT_SUM_LIMIT));
       if (flagged == 0) continue;
       float mx = -__builtin_inff();
 #pragma unroll
@@ -358,7 +368,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
                                   j_last + 1, fx);
     if (live) {
       float ls[2] = {lp[0][0] + lp[0][1], lp[1][0] + lp[1][1]};
-      if (__builtin_amdgcn_ballot_w64(!(ls[0] <= WEIGHT_SUM_LIMIT) || !(ls[1] <= WEIGHT_SUM_LIMIT)) != 0)
+      if (__builtin_amdgcn_ballot_w64(!(ls[0] <= WIDE_WEIGHT_SUM_LIMIT) ||
+                                      !(ls[1] <= WIDE_WEIGHT_SUM_LIMIT)) != 0)
         max_path(sc, wn, ls);
       l_run[0] += ls[0];
       l_run[1] += ls[1];
@@ -431,7 +442,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
       float mx = -__builtin_inff();
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s_[0][r][e]);
-      m_run[r] = pair_max(mx) * c;   // key 0 is visible to every row: finite
+      m_run[r] = pair_max(mx) * c + INIT_HEADROOM;   // key 0 is visible to every row: finite
     }
     float lp[2][2];
     phase_scores_softmax<SB, 0>(qf, s_[1], ka, s_[0], c, m_run, w_[0], lp, fx);
