@@ -85,6 +85,48 @@ def test_large_logits_small(lib):
     assert_close(to_f64(o), to_f64(lse), o_ref, lse_ref, "stress S=777")
 
 
+def _jump_and_ramp_inputs(S):
+    """Hq = 8 query heads on one KV head, D = 128, scores built on two key coordinates: key
+    150's first coordinate is 128 (every other key's is 0) and the second coordinate ramps
+    as j / 4.  Head 0 (q = 16 e0) meets a score ~181 above all earlier ones at key 150, so
+    its weights overflow against any running max set before it; head 1 (q = -16 e0) sees
+    that key ~181 below the rest; head 2 (q = 0) weights every key equally; head 3
+    (q = 16 e1) has a max that grows by ~0.35 per key, ~106 over the row; heads 4-7 mix
+    the two.  V is N(0,1)/2."""
+    rng = np.random.Generator(np.random.PCG64(131))
+    D = 128
+    q = np.zeros((S, 8, D), np.float32)
+    k = np.zeros((S, 1, D), np.float32)
+    k[150 % S, 0, 0] = 128.0
+    k[:, 0, 1] = np.arange(S, dtype=np.float32) / 4.0
+    k[:, 0, 2:] = rng.standard_normal((S, D - 2), dtype=np.float32) * 0.5
+    q[:, 0, 0], q[:, 1, 0], q[:, 3, 1] = 16.0, -16.0, 16.0
+    q[:, 4, 0], q[:, 4, 1] = 8.0, 8.0
+    q[:, 5, 0], q[:, 5, 1] = -8.0, 12.0
+    q[:, 6, 2:] = rng.standard_normal((S, D - 2), dtype=np.float32)
+    q[:, 7, 0], q[:, 7, 2:] = 4.0, rng.standard_normal((S, D - 2), dtype=np.float32)
+    # rows led by one key return about that key's value row: V at half scale keeps |O|
+    # under ~2, where the absolute O bound applies (a bf16 step there is 2^-7)
+    v = rng.standard_normal((S, 1, D), dtype=np.float32) * 0.5
+    return tuple(workloads.f32_to_bf16_bits(x) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("S", [300, 777])
+def test_score_jumps_and_ramps(lib, S):
+    """Scores that jump far above the running max (weights overflow to infinity and the
+    row takes the max path), far below it (underflow), or grow steadily over the row
+    (repeated raises), causal and bidirectional, against the oracle."""
+    q, k, v = _jump_and_ramp_inputs(S)
+    scale = workloads.default_scale(128)
+    o, lse = _run(lib, q, k, v, scale)
+    o_ref, lse_ref = oracle.gqa_causal(q, k, v, scale)
+    assert_close(to_f64(o), to_f64(lse), o_ref, lse_ref, f"jumps and ramps S={S} causal")
+    ob, lb = lib.gqa_fwd(to_device(q), to_device(k), to_device(v), causal=False,
+                         softmax_scale=scale)
+    ob_ref, lb_ref = oracle.gqa_bidirectional(q, k, v, scale)
+    assert_close(to_f64(ob), to_f64(lb), ob_ref, lb_ref, f"jumps and ramps S={S} bidirectional")
+
+
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_workload_sampled(lib, name):
     """Full-size workload on the GPU; oracle on sampled query tokens (all heads)."""
