@@ -36,8 +36,9 @@
 //    scalar branch inside the phase's assembly, so both paths share one register
 //    interface), and every wave leaves the tile loop through the same exit.
 //
-//  * O leaves through an LDS stage (the K half of the ring) so that each store writes whole
-//    256-byte rows; Q loads and O stores are non-temporal, leaving L2 to K/V.
+//  * Q comes in through LDS (ring stages 2 and 3, before tile 2 is requested) and O leaves
+//    through an LDS stage (the K half of the ring), so that every Q load and O store
+//    instruction moves whole 256-byte rows; both are non-temporal, leaving L2 to K/V.
 #pragma once
 
 #include "gqa_fwd_kernel.hpp"
@@ -181,20 +182,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
     }
   }
 
-  // ---- Q^T fragments of both row blocks (B operands), resident for the whole kernel
+  // ---- Q^T fragments of both row blocks (B operands), resident for the whole kernel; loaded
+  // through LDS in the prologue below
   bf16x8 qf[2][NDS];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    if (my_valid[r]) {
-      const uint16_t* qp = p.q + ((size_t)(start + my_tok[r]) * p.hq + my_head) * D + 8 * half;
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds)
-        qf[r][ds] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)(qp + 16 * ds)));
-    } else {
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) qf[r][ds] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-    }
-  }
 
   // ---- K/V fill: each lane one 16-byte chunk of each of its wave's 1 KB pieces; rows past
   // the sequence end read as zeros (outside the buffer range)
@@ -376,20 +366,52 @@ __global__ __launch_bounds__(C::THREADS, 1) void gqa_fwd_wide_kernel(FwdParams p
     }
   };
 
-  // ---- prologue: tiles 0 and 1 requested behind the Q loads; the empty statement below
-  // consumes every Q fragment, so the compiler waits for all vector-memory loads there (Q and
-  // both tiles, which the first phases need anyway) and knows no load of its own is pending
-  // afterwards -- it cannot see the LDS-DMA fills and would otherwise wait for them before
-  // later phases.  Tile 2 is requested after that wait.
+  // ---- prologue.  Q: the workgroup's 256 rows (token, head of the group) go global -> LDS by
+  // DMA into the ring's stages 2 and 3 (free until tile 2 is requested): 16 lanes fetch one
+  // whole 256-byte row, so every load instruction covers whole lines and can stream past the
+  // caches (non-temporal).  (A lane's MFMA fragments are every other 16 bytes of its row; read
+  // straight from global memory, one instruction touches 32 rows' lines 32 bytes each.)  Wave
+  // w loads rows 64w .. 64w+63, its own, and reads them back as B fragments; LDS row R keeps
+  // its 16-byte chunk c at position c ^ (R & 15), so the fragment reads spread over the banks.
+  // Tokens past the sequence end lie outside the buffer range and load as zeros.
+  uint16_t* const qstage = wave < 2 ? &k_lds[2][0] : &v_lds[2][0];   // 128 rows per region
+  {
+    const int ntok = min(len - q0, C::TOK_WG);           // >= 1: the block has a token
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.q + ((size_t)(start + q0) * p.hq + g * G) * D), 0,
+        ((ntok - 1) * p.hq + G) * D * 2, BUFFER_RSRC_WORD3);
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const int row = 64 * wave + 4 * n + (lane >> 4);  // the workgroup's Q row
+      const int pos = lane & 15;                        // LDS chunk this lane writes
+      const unsigned off = (unsigned)(((row / G) * p.hq + row % G) * D * 2 + ((pos ^ (row & 15)) * 16));
+      const unsigned m = __builtin_amdgcn_readfirstlane(
+          (unsigned)(uintptr_t)(lds_void*)(qstage + (64 * (wave & 1) + 4 * n) * D));
+      // as in fill_tile_lds: one wait state between the M0 write and the load
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                   :: "v"(off), "s"(qr), "s"(m) : "memory", "m0");
+#pragma clang diagnostic pop
+    }
+  }
+  // tiles 0 and 1 behind Q; every load the first phases need lands before the barrier.  The
+  // wave reads back the rows its own loads wrote, so it needs only its own wait; the barrier
+  // then also tells every wave that stages 2 and 3 are read, and tile 2 goes there (it is
+  // first read after B_1, which waits for it).
   fill_tile(0, k_lds[0], v_lds[0]);
   if (1 < n_tiles) fill_tile(1, k_lds[1], v_lds[1]);
-  asm volatile("" ::"v"(qf[0][0]), "v"(qf[0][1]), "v"(qf[0][2]), "v"(qf[0][3]), "v"(qf[0][4]),
-               "v"(qf[0][5]), "v"(qf[0][6]), "v"(qf[0][7]), "v"(qf[1][0]), "v"(qf[1][1]),
-               "v"(qf[1][2]), "v"(qf[1][3]), "v"(qf[1][4]), "v"(qf[1][5]), "v"(qf[1][6]),
-               "v"(qf[1][7]));
-  wait_vmem();
-  if (2 < n_tiles) fill_tile(2, k_lds[2], v_lds[2]);
+  // the wait as a compiler barrier too: the LDS reads below must not move above it
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int lrow = 64 * (wave & 1) + 32 * r + col;    // row in this wave's region
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+      qf[r][ds] = *(const bf16x8*)(qstage + lrow * D + (((2 * ds + half) ^ (col & 15)) * 8));
+  }
   __syncthreads();
+  if (2 < n_tiles) fill_tile(2, k_lds[2], v_lds[2]);
   if constexpr (QPRO) {
     // Q prologue, part 2, on this lane's fragments of both row blocks: elements
     // 16*ds + 8*half + 0..7 of the row; element d and its rotation partner d + D/2 sit in
