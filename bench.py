@@ -237,7 +237,8 @@ def reference(oracle, inp, w, tokens):
 def calibration_loops(stream, achieved_tflops: float, settle_s: float = 0.3,
                       launches: int = 60, iters: int = 4096) -> dict:
     """The matrix-core and exponential ceilings at the clock the GPU holds
-    (h3attn_calib_loop, one wave per SIMD, the attention kernel's occupancy).  Each loop
+    (h3attn_calib_loop, one wave per SIMD, the attention kernel's occupancy; and the MFMA
+    loop once more with two waves per SIMD, to show whether issue or power sets it).  Each loop
     first runs untimed for settle_s so the clock settles to its own load, then `launches`
     launches are timed with events; the in-kernel stamps of the last one give the clock
     and each wave's own cycles per instruction."""
@@ -246,14 +247,17 @@ def calibration_loops(stream, achieved_tflops: float, settle_s: float = 0.3,
     import causal_grouped_query_amd as h3
 
     ncu = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
-    stamps = torch.zeros((ncu * 4, 4), dtype=torch.int64, device="cuda")
-    sink = torch.empty(ncu * 256, dtype=torch.float32, device="cuda")
+    stamps = torch.zeros((2 * ncu * 4, 4), dtype=torch.int64, device="cuda")
+    sink = torch.empty(2 * ncu * 256, dtype=torch.float32, device="cuda")
     out = {}
-    for kind, name, per_iter in ((h3.CALIB_MFMA, "mfma_loop", 8),
-                                 (h3.CALIB_MFMA_ZERO, "mfma_loop_zero_operands", 8),
-                                 (h3.CALIB_EXP, "exp_loop", 16)):
+    for kind, name, per_iter, wps in ((h3.CALIB_MFMA, "mfma_loop", 8, 1),
+                                      (h3.CALIB_MFMA_ZERO, "mfma_loop_zero_operands", 8, 1),
+                                      (h3.CALIB_EXP, "exp_loop", 16, 1),
+                                      (h3.CALIB_MFMA_PAIRED, "mfma_loop_two_waves_per_simd", 8, 2)):
+        nwg = ncu * wps
+
         def run():
-            return h3.calib_loop(kind, ncu, iters, stream=stream, stamps=stamps, sink=sink)[1]
+            return h3.calib_loop(kind, nwg, iters, stream=stream, stamps=stamps, sink=sink)[1]
 
         t = time.perf_counter()
         while time.perf_counter() - t < settle_s:
@@ -267,20 +271,26 @@ def calibration_loops(stream, achieved_tflops: float, settle_s: float = 0.3,
         b.record(stream)
         b.synchronize()
         seconds = a.elapsed_time(b) * 1e-3 / launches
-        st = stamps.cpu().numpy().astype(np.float64)
+        st = stamps[: nwg * 4].cpu().numpy().astype(np.float64)
         cycles, ticks = st[:, 1] - st[:, 0], st[:, 3] - st[:, 2]
         ghz = float(np.median(cycles / (ticks / (khz * 1e3)))) / 1e9 if khz > 0 else None
-        waves = ncu * 4
+        waves = nwg * 4
         # per SIMD, from the event-timed launches at the stamped clock (launch overhead
         # included); and each wave's own loop, from its stamps
-        per_simd = (ghz * 1e9 * seconds / (iters * per_iter)) if ghz else None
+        per_simd = (ghz * 1e9 * seconds / (iters * per_iter * wps)) if ghz else None
         entry = {"cycles_per_instruction_per_simd": round(per_simd, 2) if per_simd else None,
                  "wave_loop_cycles_per_instruction":
                      round(float(np.median(cycles)) / (iters * per_iter), 2),
                  "clock_ghz": round(ghz, 3) if ghz else None,
-                 "launch_ms": round(seconds * 1e3, 4), "waves_per_simd": 1,
-                 "workgroups": ncu, "iterations": iters}
-        if kind == h3.CALIB_MFMA:
+                 "launch_ms": round(seconds * 1e3, 4), "waves_per_simd": wps,
+                 "workgroups": nwg, "iterations": iters}
+        if kind == h3.CALIB_MFMA_PAIRED:
+            tflops = waves * iters * per_iter * 32768 / seconds / 1e12
+            entry.update({"instruction": "v_mfma_f32_32x32x16_bf16, random bf16 operands, "
+                                         "two waves per SIMD",
+                          "tflops": round(tflops, 1),
+                          "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)})
+        elif kind == h3.CALIB_MFMA:
             tflops = waves * iters * per_iter * 32768 / seconds / 1e12
             entry.update({"instruction": "v_mfma_f32_32x32x16_bf16, random bf16 operands",
                           "tflops": round(tflops, 1),

@@ -35,7 +35,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # fixed scratch of h3attn_gqa_causal_splitkv_
 
 NONCAUSAL, O_HEAD_MAJOR = 1, 2   # flags of h3attn_gqa_fwd
 PROLOGUE_ROPE = 1                # flag of h3attn_qk_norm_rope
-CALIB_MFMA, CALIB_EXP, CALIB_MFMA_ZERO = 0, 1, 2   # kinds of h3attn_calib_loop
+CALIB_MFMA, CALIB_EXP, CALIB_MFMA_ZERO, CALIB_MFMA_PAIRED = 0, 1, 2, 3   # h3attn_calib_loop kinds
 
 EXPORTED = ("h3attn_gqa_causal_fwd", "h3attn_gqa_fwd", "h3attn_gqa_causal_varlen_fwd",
             "h3attn_gqa_causal_splitkv_fwd", "h3attn_gqa_causal_splitkv_workspace_bytes",
@@ -325,8 +325,8 @@ def check_cu_seqlens(cu_seqlens, total_tokens: int, max_seqlen: int) -> int:
 
 def calib_loop(kind: int, n_workgroups: int, iters: int, stream=None, device=None,
                stamps=None, sink=None):
-    """Enqueue one calibration loop (CALIB_MFMA, CALIB_MFMA_ZERO or CALIB_EXP; see
-    h3attn_calib_loop) and
+    """Enqueue one calibration loop (CALIB_MFMA, CALIB_MFMA_ZERO, CALIB_EXP or
+    CALIB_MFMA_PAIRED; see h3attn_calib_loop) and
     return (stamps, wall_clock_khz): stamps is an int64 GPU tensor [n_workgroups * 4, 4]
     (per wave: shader-clock counter before / after its loop, constant-rate counter before /
     after), filled when the stream reaches the launch; wall_clock_khz is the rate of the
@@ -490,4 +490,5 @@ __all__ = ["gqa_causal_fwd", "gqa_fwd", "gqa_causal_varlen_fwd", "gqa_causal_spl
            "splitkv_workspace_bytes", "status_string", "version", "lds_bytes", "load_library",
            "H3AttnError", "LIBRARY", "EXPORTED", "MAX_SPLITS", "NONCAUSAL", "O_HEAD_MAJOR",
            "qk_norm_rope", "gqa_causal_qnorm_rope_fwd", "PROLOGUE_ROPE", "pool_tokens",
-           "pool_tokens_out_len", "calib_loop", "CALIB_MFMA", "CALIB_EXP", "CALIB_MFMA_ZERO"]
+           "pool_tokens_out_len", "calib_loop", "CALIB_MFMA", "CALIB_EXP", "CALIB_MFMA_ZERO",
+           "CALIB_MFMA_PAIRED"]

@@ -11,7 +11,11 @@
 //           in both operands and the datapath toggles as it does on real data), or, with
 //           operand_mask 0, all-zero operands (the same instructions with a datapath that
 //           does not toggle: the clock difference between the two is the power limit);
-//   KIND 1: sixteen independent v_exp_f32 per iteration (x <- 2^-x keeps x in (0, 1]).
+//   KIND 1: sixteen independent v_exp_f32 per iteration (x <- 2^-x keeps x in (0, 1]);
+//   KIND 2: the KIND 0 loop with a 64 KB LDS reserve, so that two workgroups share a
+//           compute unit and every SIMD runs two MFMA waves when the grid has two
+//           workgroups per compute unit (a second wave does not raise the matrix core's
+//           rate on random operands if the power limit, not the issue, sets it).
 // Each wave records the shader-clock counter (s_memtime) and the constant-rate counter
 // (s_memrealtime) around its loop (in asm that waits for the values and takes the loop's
 // operands, then its results, as inputs, so that nothing moves across a stamp); every
@@ -25,6 +29,7 @@ namespace h3attn {
 
 constexpr int CALIB_THREADS = 256;             // four waves: one per SIMD of a compute unit
 constexpr int CALIB_LDS_BYTES = 96 * 1024;     // over half a CU's LDS: one workgroup per CU
+constexpr int CALIB_LDS_BYTES_PAIRED = 64 * 1024;   // two workgroups per CU
 constexpr int CALIB_MFMA_PER_ITER = 8;
 constexpr int CALIB_EXP_PER_ITER = 16;
 
@@ -51,8 +56,9 @@ __global__ __launch_bounds__(CALIB_THREADS, 1) void calib_loop_kernel(uint64_t* 
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
   typedef float f32x16 __attribute__((ext_vector_type(16)));
-  __shared__ float reserve[CALIB_LDS_BYTES / 4];
-  constexpr int STRIDE = CALIB_LDS_BYTES / 4 / CALIB_THREADS;
+  constexpr int LDS_BYTES = KIND == 2 ? CALIB_LDS_BYTES_PAIRED : CALIB_LDS_BYTES;
+  __shared__ float reserve[LDS_BYTES / 4];
+  constexpr int STRIDE = LDS_BYTES / 4 / CALIB_THREADS;
   const unsigned gid = blockIdx.x * CALIB_THREADS + threadIdx.x;
 
   // the reserved LDS is used (one word per thread) so that it stays allocated
@@ -61,7 +67,7 @@ __global__ __launch_bounds__(CALIB_THREADS, 1) void calib_loop_kernel(uint64_t* 
 
   float result = 0.0f;
   uint64_t t0, t1, r0, r1;
-  if constexpr (KIND == 0) {
+  if constexpr (KIND == 0 || KIND == 2) {
     bf16x8 a[CALIB_MFMA_PER_ITER], b[CALIB_MFMA_PER_ITER];
 #pragma unroll
     for (int i = 0; i < CALIB_MFMA_PER_ITER; ++i) {

@@ -538,7 +538,8 @@ int h3attn_calib_loop(int kind, int n_workgroups, int iters, uint64_t* stamps, f
   if (!stamps || !sink) return H3ATTN_ERR_NULL;
   if (n_workgroups < 1 || n_workgroups > 65535 || iters < 1 || iters > (1 << 24))
     return H3ATTN_ERR_SHAPE;
-  if (kind != H3ATTN_CALIB_MFMA && kind != H3ATTN_CALIB_EXP && kind != H3ATTN_CALIB_MFMA_ZERO)
+  if (kind != H3ATTN_CALIB_MFMA && kind != H3ATTN_CALIB_EXP && kind != H3ATTN_CALIB_MFMA_ZERO &&
+      kind != H3ATTN_CALIB_MFMA_PAIRED)
     return H3ATTN_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(stamps) & 7u) != 0 ||
       (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
@@ -554,6 +555,9 @@ int h3attn_calib_loop(int kind, int n_workgroups, int iters, uint64_t* stamps, f
   const hipStream_t st = static_cast<hipStream_t>(hip_stream);
   if (kind == H3ATTN_CALIB_EXP)
     hipLaunchKernelGGL((h3attn::calib_loop_kernel<1>), dim3(n_workgroups),
+                       dim3(h3attn::CALIB_THREADS), 0, st, stamps, sink, iters, 0xFFFFu);
+  else if (kind == H3ATTN_CALIB_MFMA_PAIRED)
+    hipLaunchKernelGGL((h3attn::calib_loop_kernel<2>), dim3(n_workgroups),
                        dim3(h3attn::CALIB_THREADS), 0, st, stamps, sink, iters, 0xFFFFu);
   else   // one instance for both operand sets: the mask is a run-time value
     hipLaunchKernelGGL((h3attn::calib_loop_kernel<0>), dim3(n_workgroups),

@@ -298,10 +298,14 @@ H3ATTN_API int h3attn_pool_tokens_out_len(int T, int begin, int end, int factor)
  *     does not toggle draws less power; the clock difference to H3ATTN_CALIB_MFMA shows
  *     how much the power limit sets the rate on real data);
  *   kind H3ATTN_CALIB_EXP: each wave issues iters * 16 v_exp_f32 on sixteen independent
- *     fp32 values.
- * n_workgroups workgroups of 256 threads (four waves); each reserves 96 KB of LDS, so no
- * compute unit holds two of them: with n_workgroups equal to the number of compute units
- * every SIMD runs one wave, the attention kernel's occupancy.
+ *     fp32 values;
+ *   kind H3ATTN_CALIB_MFMA_PAIRED: the H3ATTN_CALIB_MFMA loop in workgroups that reserve
+ *     64 KB of LDS instead of 96 KB, so that a compute unit holds two: with n_workgroups
+ *     twice the number of compute units every SIMD runs two MFMA waves.
+ * n_workgroups workgroups of 256 threads (four waves); except for
+ * H3ATTN_CALIB_MFMA_PAIRED each reserves 96 KB of LDS, so no compute unit holds two of
+ * them: with n_workgroups equal to the number of compute units every SIMD runs one wave,
+ * the attention kernel's occupancy.
  *   stamps  DEVICE uint64 [n_workgroups * 4][4]: per wave, the shader-clock counter
  *           (s_memtime) before and after its loop, then the constant-rate counter
  *           (s_memrealtime) before and after;
@@ -315,6 +319,7 @@ H3ATTN_API int h3attn_pool_tokens_out_len(int T, int begin, int end, int factor)
 #define H3ATTN_CALIB_MFMA 0
 #define H3ATTN_CALIB_EXP 1
 #define H3ATTN_CALIB_MFMA_ZERO 2
+#define H3ATTN_CALIB_MFMA_PAIRED 3
 H3ATTN_API int h3attn_calib_loop(int kind, int n_workgroups, int iters, uint64_t* stamps,
                                  float* sink, int* wall_clock_khz, void* hip_stream);
 

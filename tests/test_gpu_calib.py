@@ -2,7 +2,8 @@
 through the C ABI entry h3attn_calib_loop (needs a gfx950 GPU): every wave records its
 stamps, the counters move forward, and the cycles per instruction fall in the range the
 instruction can take (a v_mfma_f32_32x32x16_bf16 occupies the matrix core for 32 cycles
-at one wave per SIMD; a v_exp_f32 of a whole wave takes a few to a few tens of cycles)."""
+at one wave per SIMD and 48 per wave at two; a v_exp_f32 of a whole wave takes a few to a
+few tens of cycles).  The paired kind runs two workgroups per compute unit."""
 
 from __future__ import annotations
 
@@ -29,17 +30,18 @@ def _announce(request):
     yield
 
 
-@pytest.mark.parametrize("kind,per_iter,lo,hi", [(0, 8, 30.0, 80.0), (2, 8, 30.0, 80.0),
-                                                 (1, 16, 2.0, 64.0)])
-def test_calib_loop_stamps(h3, kind, per_iter, lo, hi):
+@pytest.mark.parametrize("kind,per_iter,lo,hi,wps", [(0, 8, 30.0, 80.0, 1), (2, 8, 30.0, 80.0, 1),
+                                                     (1, 16, 2.0, 64.0, 1),
+                                                     (3, 8, 30.0, 120.0, 2)])
+def test_calib_loop_stamps(h3, kind, per_iter, lo, hi, wps):
     import torch
 
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     iters = 256
-    stamps, khz = h3.calib_loop(kind, ncu, iters)
+    stamps, khz = h3.calib_loop(kind, wps * ncu, iters)
     torch.cuda.synchronize()
     st = stamps.cpu().numpy()
-    assert st.shape == (ncu * 4, 4)
+    assert st.shape == (wps * ncu * 4, 4)
     assert khz > 0
     cycles, ticks = st[:, 1] - st[:, 0], st[:, 3] - st[:, 2]
     assert (cycles > 0).all() and (ticks > 0).all()          # every wave wrote its stamps
