@@ -89,7 +89,8 @@ def test_splitkv_large_logits(lib):
     assert_close(to_f64(o), to_f64(lse), o_ref, lse_ref, "split-KV stress S=777")
 
 
-@pytest.mark.parametrize("S,Hq,Hkv,D,ns", [(300, 8, 2, 128, 3), (600, 8, 8, 64, 4)])
+@pytest.mark.parametrize("S,Hq,Hkv,D,ns", [(300, 8, 2, 128, 3), (600, 8, 8, 64, 4),
+                                            (300, 16, 2, 128, 3), (200, 8, 1, 128, 5)])
 def test_splitkv_partials_match_oracle_key_ranges(lib, S, Hq, Hkv, D, ns):
     """Each split's partial O and LSE in the workspace equal the oracle's attention over
     that split's key range; rows with no key in the range hold LSE = -inf."""
